@@ -1,0 +1,301 @@
+"""Python binding of libsparse_attn (block-sparse video attention forward for
+MI355X / gfx950).
+
+A thin ctypes layer with the same names as the C-ABI in
+include/sparse_attn.h: it marshals torch tensors (device memory) and streams
+into pointers and raises SparseAttnError on a non-zero status.  Every step of
+the computation runs in the HIP library; there is no fallback path.  The
+library must have been built (block_sparse_attention_major_amd/build.py);
+importing this module fails loudly if it is missing.
+
+``SparseAttention`` is a small convenience wrapper that allocates the mask
+buffer and workspace with torch and calls the same entry points.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
+        "or python block_sparse_attention_major_amd/build.py)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SPARSE_ATTN_OK = 0
+SPARSE_ATTN_INVALID_ARG = 1
+SPARSE_ATTN_UNSUPPORTED = 2
+SPARSE_ATTN_BAD_MASK = 3
+SPARSE_ATTN_WORKSPACE_TOO_SMALL = 4
+SPARSE_ATTN_NO_MASK = 5
+SPARSE_ATTN_HIP_ERROR = 6
+
+SPARSE_ATTN_F32 = 0
+SPARSE_ATTN_BF16 = 1
+SPARSE_ATTN_MASK_BITMAP = 0
+SPARSE_ATTN_MASK_DUAL_WINDOW = 1
+SPARSE_ATTN_LAYOUT_ROWS = 0
+SPARSE_ATTN_LAYOUT_TILE_COLUMNS = 1
+SPARSE_ATTN_KERNEL_MFMA_BF16 = 0
+SPARSE_ATTN_KERNEL_GENERIC = 1
+SPARSE_ATTN_MAX_GROUPS = 8
+
+EXPORTED = [
+    "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_layout", "sparse_attn_mask_bytes",
+    "sparse_attn_workspace_bytes", "sparse_attn_set_mask", "sparse_attn_forward",
+    "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
+    "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
+    "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
+]
+
+
+class sparse_attn_config(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("grid", ctypes.c_int32 * 3), ("tile", ctypes.c_int32 * 3),
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+
+
+class sparse_attn_window_group(ctypes.Structure):
+    _fields_ = [("dt_lo", ctypes.c_int32), ("dt_hi", ctypes.c_int32),
+                ("ry", ctypes.c_int32 * 2), ("rx", ctypes.c_int32 * 2)]
+
+
+class sparse_attn_mask(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("bitmap", ctypes.c_void_p),
+                ("groups", ctypes.c_void_p), ("groups_per_head", ctypes.c_void_p),
+                ("max_nnz", ctypes.c_int64)]
+
+
+class sparse_attn_layout_info(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("tiles", ctypes.c_int64),
+                ("tile_grid", ctypes.c_int32 * 3), ("tile_volume", ctypes.c_int32),
+                ("slots", ctypes.c_int64), ("kernel", ctypes.c_int32), ("v_layout", ctypes.c_int32),
+                ("ws_offset_q", ctypes.c_size_t), ("ws_offset_k", ctypes.c_size_t),
+                ("ws_offset_v", ctypes.c_size_t), ("ws_offset_o", ctypes.c_size_t),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P = ctypes.POINTER
+_sigs = {
+    "sparse_attn_create": ([_P(sparse_attn_config), _P(_vp)], ctypes.c_int),
+    "sparse_attn_destroy": ([_vp], None),
+    "sparse_attn_layout": ([_vp, _P(sparse_attn_layout_info)], ctypes.c_int),
+    "sparse_attn_mask_bytes": ([_vp, _i64, _P(_sz)], ctypes.c_int),
+    "sparse_attn_workspace_bytes": ([_vp, _P(_sz)], ctypes.c_int),
+    "sparse_attn_set_mask": ([_vp, _P(sparse_attn_mask), _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_permute_inputs": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_attend": ([_vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_unpermute_output": ([_vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    "sparse_attn_permute": ([_vp, _vp, _vp, _i32, _vp], ctypes.c_int),
+    "sparse_attn_unpermute": ([_vp, _vp, _vp, _vp], ctypes.c_int),
+    "sparse_attn_read_index_lists": ([_vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
+    "sparse_attn_mask_info": ([_vp, _P(_i64), _P(_i32), _vp], ctypes.c_int),
+    "sparse_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "sparse_attn_last_error": ([_vp], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{sparse_attn_status_string(status)} ({status}): {message}")
+        self.status = status
+        self.message = message
+
+
+def sparse_attn_status_string(status):
+    return _lib.sparse_attn_status_string(int(status)).decode()
+
+
+def sparse_attn_last_error(h=None):
+    return _lib.sparse_attn_last_error(h.ptr if h is not None else None).decode()
+
+
+class Handle:
+    """Owns a sparse_attn_handle*; destroyed with sparse_attn_destroy."""
+
+    def __init__(self, ptr, cfg):
+        self.ptr = ptr
+        self.cfg = cfg
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            _lib.sparse_attn_destroy(self.ptr)
+            self.ptr = None
+
+
+def _check(status, h=None):
+    if status != SPARSE_ATTN_OK:
+        raise SparseAttnError(status, sparse_attn_last_error(h))
+
+
+def _dptr(t, name):
+    """Device pointer of a torch tensor (or None / raw int)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0):
+    """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32."""
+    if isinstance(dtype, str):
+        dtype = {"bf16": SPARSE_ATTN_BF16, "f32": SPARSE_ATTN_F32}[dtype]
+    cfg = sparse_attn_config(int(heads), int(head_dim), (ctypes.c_int32 * 3)(*grid),
+                             (ctypes.c_int32 * 3)(*tile), int(dtype), float(softmax_scale))
+    out = _vp()
+    st = _lib.sparse_attn_create(ctypes.byref(cfg), ctypes.byref(out))
+    if st != SPARSE_ATTN_OK:
+        raise SparseAttnError(st, sparse_attn_last_error(None))
+    return Handle(out.value, cfg)
+
+
+def sparse_attn_destroy(h):
+    if h.ptr:
+        _lib.sparse_attn_destroy(h.ptr)
+        h.ptr = None
+
+
+def sparse_attn_layout(h):
+    info = sparse_attn_layout_info()
+    _check(_lib.sparse_attn_layout(h.ptr, ctypes.byref(info)), h)
+    return {f: (list(getattr(info, f)) if f == "tile_grid" else getattr(info, f))
+            for f, _ in sparse_attn_layout_info._fields_}
+
+
+def sparse_attn_mask_bytes(h, max_nnz=0):
+    n = _sz()
+    _check(_lib.sparse_attn_mask_bytes(h.ptr, int(max_nnz), ctypes.byref(n)), h)
+    return n.value
+
+
+def sparse_attn_workspace_bytes(h):
+    n = _sz()
+    _check(_lib.sparse_attn_workspace_bytes(h.ptr, ctypes.byref(n)), h)
+    return n.value
+
+
+def sparse_attn_set_mask(h, mask_buf, bitmap=None, groups=None, groups_per_head=None, max_nnz=0,
+                         stream=None):
+    """Bitmap mask: `bitmap` is a device uint8 tensor [heads, nT, nT].
+    Dual-window mask: `groups` int32 [G, 6] rows (dt_lo, dt_hi, ry0, ry1, rx0,
+    rx1) and `groups_per_head` int32 [heads], host arrays."""
+    m = sparse_attn_mask()
+    keep = []
+    if bitmap is not None:
+        m.kind = SPARSE_ATTN_MASK_BITMAP
+        m.bitmap = _dptr(bitmap, "bitmap")
+    else:
+        g = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 6)
+        gph = np.ascontiguousarray(groups_per_head, dtype=np.int32)
+        keep += [g, gph]
+        m.kind = SPARSE_ATTN_MASK_DUAL_WINDOW
+        m.groups = g.ctypes.data
+        m.groups_per_head = gph.ctypes.data
+    m.max_nnz = int(max_nnz)
+    _check(_lib.sparse_attn_set_mask(h.ptr, ctypes.byref(m), _dptr(mask_buf, "mask_buf"),
+                                     _nbytes(mask_buf), _stream(stream)), h)
+    del keep
+
+
+def sparse_attn_forward(h, q, k, v, o, ws, stream=None):
+    _check(_lib.sparse_attn_forward(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"), _dptr(o, "o"),
+                                    _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_permute_inputs(h, q, k, v, ws, stream=None):
+    _check(_lib.sparse_attn_permute_inputs(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"),
+                                           _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_attend(h, ws, stream=None):
+    _check(_lib.sparse_attn_attend(h.ptr, _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_unpermute_output(h, ws, o, stream=None):
+    _check(_lib.sparse_attn_unpermute_output(h.ptr, _dptr(ws, "ws"), _nbytes(ws), _dptr(o, "o"),
+                                             _stream(stream)), h)
+
+
+def sparse_attn_permute(h, src, dst, layout=SPARSE_ATTN_LAYOUT_ROWS, stream=None):
+    _check(_lib.sparse_attn_permute(h.ptr, _dptr(src, "src"), _dptr(dst, "dst"), int(layout),
+                                    _stream(stream)), h)
+
+
+def sparse_attn_unpermute(h, src, dst, stream=None):
+    _check(_lib.sparse_attn_unpermute(h.ptr, _dptr(src, "src"), _dptr(dst, "dst"), _stream(stream)), h)
+
+
+def sparse_attn_read_index_lists(h, row_ptr, cols, order, stream=None):
+    _check(_lib.sparse_attn_read_index_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
+                                             cols.numel() if cols is not None else 0,
+                                             _dptr(order, "order"), _stream(stream)), h)
+
+
+def sparse_attn_mask_info(h, stream=None):
+    nnz, ovf = _i64(), _i32()
+    _check(_lib.sparse_attn_mask_info(h.ptr, ctypes.byref(nnz), ctypes.byref(ovf), _stream(stream)), h)
+    return nnz.value, bool(ovf.value)
+
+
+class SparseAttention:
+    """Convenience wrapper: one handle plus torch-allocated mask buffer and
+    workspace on `device`."""
+
+    def __init__(self, heads, head_dim, grid, tile, dtype="bf16", softmax_scale=0.0, device="cuda"):
+        import torch
+        self.torch = torch
+        self.h = sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale)
+        self.layout = sparse_attn_layout(self.h)
+        self.device = device
+        self.heads, self.head_dim = heads, head_dim
+        self.ws = torch.empty(sparse_attn_workspace_bytes(self.h), dtype=torch.uint8, device=device)
+        self.mask_buf = None
+
+    def _mask_buf(self, max_nnz):
+        need = sparse_attn_mask_bytes(self.h, max_nnz)
+        if self.mask_buf is None or self.mask_buf.numel() < need:
+            self.mask_buf = self.torch.empty(need, dtype=self.torch.uint8, device=self.device)
+        return self.mask_buf
+
+    def set_mask_bitmap(self, bitmap, max_nnz=0, stream=None):
+        sparse_attn_set_mask(self.h, self._mask_buf(max_nnz), bitmap=bitmap, max_nnz=max_nnz,
+                             stream=stream)
+
+    def set_mask_windows(self, groups, groups_per_head, max_nnz=0, stream=None):
+        sparse_attn_set_mask(self.h, self._mask_buf(max_nnz), groups=groups,
+                             groups_per_head=groups_per_head, max_nnz=max_nnz, stream=stream)
+
+    def forward(self, q, k, v, o=None, stream=None):
+        if o is None:
+            o = self.torch.empty_like(q)
+        sparse_attn_forward(self.h, q, k, v, o, self.ws, stream)
+        return o

@@ -1,0 +1,109 @@
+// Internal definitions shared by the HIP kernels and the host library.
+//
+// Tile layout (Compact Attention page, abstract: one tile-aligned mask
+// family; Fig. 3 caption: masks run in block-sparse attention kernels).  The
+// T x H x W token grid (raster token id n = (t H + y) W + x) is cut into
+// tt x th x tw tiles, numbered raster over the tile grid (nt, ny, nx).  Tiles
+// at the far edges are clipped.  Tile tau owns slots [tau B, tau B + B) of
+// the tile-major layout, B = tt th tw; its c_tau real tokens fill the first
+// c_tau slots in raster order over the clipped tile, and the remaining slots
+// are empty (zero in permuted inputs, never read back from outputs).  One
+// tile is one block of the attention kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct Layout {
+    int T, H, W;      // token grid
+    int tt, th, tw;   // tile shape
+    int nt, ny, nx;   // tile grid
+    int nT;           // tiles
+    int B;            // slots per tile
+    int heads;
+    int D;            // head dim
+    long long N;      // tokens
+    long long Npad;   // slots = nT * B
+};
+
+// Clipped extents of tile tau along t, y, x.
+struct TileBox {
+    int a, b, e;      // tile coordinates
+    int et, ey, ex;   // clipped extents
+};
+
+__host__ __device__ inline TileBox tile_box(const Layout &L, int tau)
+{
+    TileBox r;
+    r.a = tau / (L.ny * L.nx);
+    r.b = (tau / L.nx) % L.ny;
+    r.e = tau % L.nx;
+    r.et = min(L.tt, L.T - r.a * L.tt);
+    r.ey = min(L.th, L.H - r.b * L.th);
+    r.ex = min(L.tw, L.W - r.e * L.tw);
+    return r;
+}
+
+__host__ __device__ inline int tile_real_count(const Layout &L, int tau)
+{
+    TileBox r = tile_box(L, tau);
+    return r.et * r.ey * r.ex;
+}
+
+// Round a byte count up to a 256-byte boundary.
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (each returns the launch status).
+
+// Raster rows [heads][N][D] -> tile-major rows [heads][Npad][D], empty slots 0.
+hipError_t launch_permute_rows(const Layout &L, int elem_bytes, const void *src, void *dst,
+                               hipStream_t s);
+// Raster rows -> per-tile transposed [heads][nT][D][B] (bf16 only).
+hipError_t launch_permute_tile_columns(const Layout &L, const void *src, void *dst, hipStream_t s);
+// Tile-major rows [heads][Npad][D] -> raster rows [heads][N][D].
+hipError_t launch_unpermute_rows(const Layout &L, int elem_bytes, const void *src, void *dst,
+                                 hipStream_t s);
+
+// Compiled mask buffers inside the caller's mask buffer.
+struct MaskBuffers {
+    int *row_ptr;   // [R + 1]
+    int *len;       // [R]
+    int *order;     // [R]
+    int *chunk;     // [nchunks][nT + 1]: per-chunk length histogram, then bases
+    int *bucket;    // [nT + 1]
+    int *status;    // [0] = nnz, [1] = overflow flag
+    int *groups;    // [heads * MAX_GROUPS][6]
+    int *group_off; // [heads + 1]
+    int *cols;      // [cap]
+    long long cap;
+    int R;
+    int nchunks;
+};
+
+constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
+
+hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
+                               const MaskBuffers &mb, hipStream_t s);
+
+struct AttnParams {
+    const void *q;      // tile-major rows
+    const void *k;      // tile-major rows
+    const void *v;      // tile-major rows (generic) or tile columns (MFMA)
+    void *o;            // tile-major rows
+    const int *row_ptr;
+    const int *cols;
+    const int *order;
+    long long cap;      // valid entries of cols
+    float scale_log2;   // softmax scale * log2(e)
+};
+
+// bf16 matrix-core kernel: B == 128, D in {64, 128}.
+hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
+// fp32 vector-ALU kernel for any supported shape; elem_bytes 4 (fp32) or 2 (bf16).
+hipError_t launch_attention_generic(const Layout &L, int elem_bytes, const AttnParams &p,
+                                    hipStream_t s);
+
+}  // namespace sa

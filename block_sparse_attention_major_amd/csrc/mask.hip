@@ -1,0 +1,234 @@
+// Mask compiler: tile bitmap or dual-window spec -> per-query-tile index
+// lists of kept key tiles, and a longest-first work order.
+//
+// The pages' pipeline precomputes a mask per head and loads it into the
+// block-sparse attention kernel, reusing it over several denoising steps
+// (Compact Attention page, Fig. 3 caption), so this runs once per mask.
+// Dual windows follow the reading given at sparse_attn_window_group: keep
+// (i -> j) when the tile-t distance lies in a group and the (y, x) offset
+// lies inside one of that group's two centred windows (Fig. 1 caption part
+// (3), Fig. 4 caption).
+//
+// Every output is deterministic: row lengths and histograms are counts, the
+// index list is written by an ordered ballot compaction, and the work order
+// is a stable counting sort by decreasing length.
+//
+// Rows r = h nT + i.  Stages:
+//   zero   : clear the per-chunk length histograms and the status words
+//   count  : one wave per row -> len[r]; histogram of lengths per 256-row chunk
+//   scan   : one workgroup -> row_ptr (exclusive sum of len), nnz, overflow;
+//            bucket starts of each length in decreasing order; per-chunk bases
+//   fill   : one wave per row -> ascending key-tile ids
+//   order  : one workgroup per chunk -> order[base + rank among equal lengths]
+#include "common.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kWave = 64;
+
+struct RowCtx {
+    int h, ai, bi, ei;
+    int g0, g1;  // group range of head h
+};
+
+__device__ __forceinline__ RowCtx row_ctx(const Layout &L, const MaskBuffers &mb, int r)
+{
+    RowCtx c;
+    c.h = r / L.nT;
+    const int i = r - c.h * L.nT;
+    c.ai = i / (L.ny * L.nx);
+    c.bi = (i / L.nx) % L.ny;
+    c.ei = i % L.nx;
+    c.g0 = mb.group_off[c.h];
+    c.g1 = mb.group_off[c.h + 1];
+    return c;
+}
+
+__device__ __forceinline__ bool window_keeps(const Layout &L, const MaskBuffers &mb,
+                                             const RowCtx &c, int j)
+{
+    const int aj = j / (L.ny * L.nx), bj = (j / L.nx) % L.ny, ej = j % L.nx;
+    const int dt = abs(c.ai - aj), dy = abs(c.bi - bj), dx = abs(c.ei - ej);
+    for (int g = c.g0; g < c.g1; ++g) {
+        const int *G = mb.groups + 6 * g;  // dt_lo, dt_hi, ry0, ry1, rx0, rx1
+        if (dt < G[0] || (G[1] >= 0 && dt > G[1]))
+            continue;
+        if (G[2] >= 0 && G[4] >= 0 && dy <= G[2] && dx <= G[4])
+            return true;
+        if (G[3] >= 0 && G[5] >= 0 && dy <= G[3] && dx <= G[5])
+            return true;
+    }
+    return false;
+}
+
+template <int KIND>
+__device__ __forceinline__ bool keeps(const Layout &L, const MaskBuffers &mb,
+                                      const uint8_t *__restrict__ bitmap, const RowCtx &c, int r,
+                                      int j)
+{
+    if (KIND == 0)
+        return bitmap[(long long)r * L.nT + j] != 0;
+    return window_keeps(L, mb, c, j);
+}
+
+__global__ void zero_kernel(int *__restrict__ p, long long n)
+{
+    for (long long u = blockIdx.x * (long long)blockDim.x + threadIdx.x; u < n;
+         u += (long long)gridDim.x * blockDim.x)
+        p[u] = 0;
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void count_kernel(Layout L, MaskBuffers mb,
+                                                    const uint8_t *__restrict__ bitmap)
+{
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= mb.R)
+        return;
+    const int lane = threadIdx.x & 63;
+    const RowCtx c = row_ctx(L, mb, r);
+    int n = 0;
+    for (int j = lane; j < L.nT; j += kWave)
+        n += keeps<KIND>(L, mb, bitmap, c, r, j) ? 1 : 0;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        n += __shfl_xor(n, off);
+    if (lane == 0) {
+        mb.len[r] = n;
+        atomicAdd(&mb.chunk[(long long)(r / kMaskChunk) * (L.nT + 1) + n], 1);
+    }
+}
+
+// Exclusive scan of x[0..n) into y[0..n) (y may alias x) by one workgroup of
+// 1024 threads; returns the total to every thread.  `rev` reads and writes
+// x[n - 1 - u] for u = 0..n-1 (a scan in decreasing index order).
+__device__ long long block_exclusive_scan(const int *x, int *y, long long n, bool rev,
+                                          long long *lds)
+{
+    const int t = threadIdx.x, nt = blockDim.x;
+    const long long seg = (n + nt - 1) / nt;
+    const long long lo = min(n, t * seg), hi = min(n, lo + seg);
+    long long s = 0;
+    for (long long u = lo; u < hi; ++u)
+        s += x[rev ? n - 1 - u : u];
+    lds[t] = s;
+    __syncthreads();
+    // Hillis-Steele inclusive scan of the per-thread sums.
+    for (int off = 1; off < nt; off <<= 1) {
+        long long add = t >= off ? lds[t - off] : 0;
+        __syncthreads();
+        lds[t] += add;
+        __syncthreads();
+    }
+    long long run = lds[t] - s;
+    const long long total = lds[nt - 1];
+    for (long long u = lo; u < hi; ++u) {
+        const long long idx = rev ? n - 1 - u : u;
+        const int v = x[idx];
+        y[idx] = (int)run;
+        run += v;
+    }
+    __syncthreads();
+    return total;
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(Layout L, MaskBuffers mb)
+{
+    __shared__ long long lds[1024];
+    // Row offsets.
+    const long long nnz = block_exclusive_scan(mb.len, mb.row_ptr, mb.R, false, lds);
+    if (threadIdx.x == 0) {
+        mb.row_ptr[mb.R] = (int)nnz;
+        mb.status[0] = (int)nnz;
+        mb.status[1] = nnz > mb.cap ? 1 : 0;
+    }
+    // Rows per length, then bucket starts in decreasing length order.
+    const int nL = L.nT + 1;
+    for (int len = threadIdx.x; len < nL; len += blockDim.x) {
+        int tot = 0;
+        for (int c = 0; c < mb.nchunks; ++c)
+            tot += mb.chunk[(long long)c * nL + len];
+        mb.bucket[len] = tot;
+    }
+    __threadfence_block();
+    __syncthreads();
+    block_exclusive_scan(mb.bucket, mb.bucket, nL, true, lds);
+    __threadfence_block();
+    __syncthreads();
+    // Base of each (chunk, length): bucket start + rows of that length in
+    // earlier chunks.
+    for (int len = threadIdx.x; len < nL; len += blockDim.x) {
+        int run = mb.bucket[len];
+        for (int c = 0; c < mb.nchunks; ++c) {
+            int *p = &mb.chunk[(long long)c * nL + len];
+            const int x = *p;
+            *p = run;
+            run += x;
+        }
+    }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(256) void fill_kernel(Layout L, MaskBuffers mb,
+                                                   const uint8_t *__restrict__ bitmap)
+{
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= mb.R)
+        return;
+    const int lane = threadIdx.x & 63;
+    const RowCtx c = row_ctx(L, mb, r);
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    long long base = mb.row_ptr[r];
+    for (int j0 = 0; j0 < L.nT; j0 += kWave) {
+        const int j = j0 + lane;
+        const bool keep = j < L.nT && keeps<KIND>(L, mb, bitmap, c, r, j);
+        const unsigned long long bits = __ballot(keep);
+        const long long pos = base + __popcll(bits & below);
+        if (keep && pos < mb.cap)
+            mb.cols[pos] = j;
+        base += __popcll(bits);
+    }
+}
+
+__global__ __launch_bounds__(kMaskChunk) void order_kernel(Layout L, MaskBuffers mb)
+{
+    __shared__ int lens[kMaskChunk];
+    const int t = threadIdx.x;
+    const int r = blockIdx.x * kMaskChunk + t;
+    const int len = r < mb.R ? mb.len[r] : -1;
+    lens[t] = len;
+    __syncthreads();
+    if (r >= mb.R)
+        return;
+    int rank = 0;
+    for (int u = 0; u < t; ++u)
+        rank += lens[u] == len ? 1 : 0;
+    const int base = mb.chunk[(long long)blockIdx.x * (L.nT + 1) + len];
+    mb.order[base + rank] = r;
+}
+
+}  // namespace
+
+hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
+                               const MaskBuffers &mb, hipStream_t s)
+{
+    const long long nchunk_words = (long long)mb.nchunks * (L.nT + 1);
+    hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, s, mb.chunk, nchunk_words);
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, mb.status, 16ll);
+    const dim3 rows_grid((mb.R + 3) / 4);
+    if (kind == 0)
+        hipLaunchKernelGGL(count_kernel<0>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
+    else
+        hipLaunchKernelGGL(count_kernel<1>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, L, mb);
+    if (kind == 0)
+        hipLaunchKernelGGL(fill_kernel<0>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
+    else
+        hipLaunchKernelGGL(fill_kernel<1>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
+    hipLaunchKernelGGL(order_kernel, dim3(mb.nchunks), dim3(kMaskChunk), 0, s, L, mb);
+    return hipGetLastError();
+}
+
+}  // namespace sa

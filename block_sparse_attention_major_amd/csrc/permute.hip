@@ -1,0 +1,130 @@
+// Tile-major token permutation and its inverse.
+//
+// A tile's real tokens are et * ey runs of ex tokens that are contiguous in
+// raster order, and land in contiguous slots.  So one workgroup per
+// (head, tile) copies each run as one contiguous block of 16-byte vectors:
+// no per-element index arithmetic, fully coalesced reads and writes.  Both
+// kernels are bound by HBM bandwidth.
+#include "common.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// Copies one run of `nvec` 16-byte vectors.
+__device__ __forceinline__ void copy_run(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                         int nvec)
+{
+    for (int v = threadIdx.x; v < nvec; v += kThreads)
+        dst[v] = src[v];
+}
+
+// dir = 0: raster -> tile-major (and zero the empty slots); dir = 1: back.
+template <int DIR>
+__global__ __launch_bounds__(kThreads) void permute_rows_kernel(Layout L, int vpr,
+                                                                const uint4 *__restrict__ src,
+                                                                uint4 *__restrict__ dst)
+{
+    const int h = blockIdx.x / L.nT;
+    const int tau = blockIdx.x - h * L.nT;
+    const TileBox bx = tile_box(L, tau);
+    const long long raster0 = (long long)h * L.N;
+    const long long slot0 = (long long)h * L.Npad + (long long)tau * L.B;
+    for (int lt = 0; lt < bx.et; ++lt) {
+        for (int ly = 0; ly < bx.ey; ++ly) {
+            const int t = bx.a * L.tt + lt, y = bx.b * L.th + ly, x = bx.e * L.tw;
+            const long long n0 = raster0 + ((long long)t * L.H + y) * L.W + x;
+            const long long p0 = slot0 + (long long)(lt * bx.ey + ly) * bx.ex;
+            if (DIR == 0)
+                copy_run(src + n0 * vpr, dst + p0 * vpr, bx.ex * vpr);
+            else
+                copy_run(src + p0 * vpr, dst + n0 * vpr, bx.ex * vpr);
+        }
+    }
+    if (DIR == 0) {
+        const int c = bx.et * bx.ey * bx.ex;
+        uint4 *pad = dst + (slot0 + c) * vpr;
+        const int nvec = (L.B - c) * vpr;
+        for (int v = threadIdx.x; v < nvec; v += kThreads)
+            pad[v] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// Raster bf16 rows -> per-tile transposed block [D][B]: row f of tile tau
+// holds feature f of slots 0..B-1 (empty slots 0).  The tile passes through
+// LDS as [B][D + 2] so the transposed reads spread over banks.
+template <int D>
+__global__ __launch_bounds__(kThreads) void permute_tile_columns_kernel(
+    Layout L, const uint16_t *__restrict__ src, uint16_t *__restrict__ dst)
+{
+    constexpr int LD = D + 2;
+    __shared__ uint16_t tileT[128 * LD];
+    const int h = blockIdx.x / L.nT;
+    const int tau = blockIdx.x - h * L.nT;
+    const TileBox bx = tile_box(L, tau);
+    const int c = bx.et * bx.ey * bx.ex;
+    const int B = L.B;
+    // Gather the real rows (zero the empty ones) into LDS, 4 bytes at a time.
+    constexpr int WPR = D / 2;  // 32-bit words per row
+    for (int u = threadIdx.x; u < B * WPR; u += kThreads) {
+        const int slot = u / WPR, w = u - slot * WPR;
+        uint32_t val = 0;
+        if (slot < c) {
+            const int ex = bx.ex, ey = bx.ey;
+            const int lt = slot / (ey * ex), ly = (slot / ex) % ey, lx = slot % ex;
+            const long long n = ((long long)(bx.a * L.tt + lt) * L.H + (bx.b * L.th + ly)) * L.W +
+                                (bx.e * L.tw + lx);
+            val = reinterpret_cast<const uint32_t *>(src + ((long long)h * L.N + n) * D)[w];
+        }
+        tileT[slot * LD + 2 * w] = (uint16_t)(val & 0xFFFF);
+        tileT[slot * LD + 2 * w + 1] = (uint16_t)(val >> 16);
+    }
+    __syncthreads();
+    // Write row f: B slots, 8 per 16-byte vector.
+    const int vpr = B / 8;
+    uint16_t *out = dst + ((long long)h * L.nT + tau) * D * B;
+    for (int u = threadIdx.x; u < D * vpr; u += kThreads) {
+        const int f = u / vpr, g = u - f * vpr;
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            w[k] = (uint32_t)tileT[(8 * g + 2 * k) * LD + f] |
+                   ((uint32_t)tileT[(8 * g + 2 * k + 1) * LD + f] << 16);
+        reinterpret_cast<uint4 *>(out + (long long)f * B)[g] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_permute_rows(const Layout &L, int elem_bytes, const void *src, void *dst,
+                               hipStream_t s)
+{
+    const int vpr = L.D * elem_bytes / 16;
+    hipLaunchKernelGGL(permute_rows_kernel<0>, dim3(L.heads * L.nT), dim3(kThreads), 0, s, L, vpr,
+                       (const uint4 *)src, (uint4 *)dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpermute_rows(const Layout &L, int elem_bytes, const void *src, void *dst,
+                                 hipStream_t s)
+{
+    const int vpr = L.D * elem_bytes / 16;
+    hipLaunchKernelGGL(permute_rows_kernel<1>, dim3(L.heads * L.nT), dim3(kThreads), 0, s, L, vpr,
+                       (const uint4 *)src, (uint4 *)dst);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute_tile_columns(const Layout &L, const void *src, void *dst, hipStream_t s)
+{
+    if (L.D == 128)
+        hipLaunchKernelGGL(permute_tile_columns_kernel<128>, dim3(L.heads * L.nT), dim3(kThreads), 0,
+                           s, L, (const uint16_t *)src, (uint16_t *)dst);
+    else
+        hipLaunchKernelGGL(permute_tile_columns_kernel<64>, dim3(L.heads * L.nT), dim3(kThreads), 0,
+                           s, L, (const uint16_t *)src, (uint16_t *)dst);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,536 @@
+// Host side of the C-ABI: argument checks, layout planning, buffer carving
+// and kernel orchestration.  No device memory is allocated here: every device
+// buffer is the caller's.  Every check runs before the first enqueue.
+#include "sparse_attn.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+struct sparse_attn_handle {
+    sparse_attn_config cfg;
+    sa::Layout L;
+    int elem_bytes;
+    int kernel;
+    float scale;
+    // compiled mask
+    bool has_mask = false;
+    sa::MaskBuffers mb{};
+    // host copy of the last dual-window spec (source of the upload)
+    std::vector<int32_t> spec;
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_create_err;
+
+int fail(sparse_attn_handle *h, int code, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (h)
+        h->err = buf;
+    else
+        g_create_err = buf;
+    return code;
+}
+
+int hip_fail(sparse_attn_handle *h, hipError_t e, const char *what)
+{
+    return fail(h, SPARSE_ATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb)
+{
+    const auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+// Mask-buffer carving.
+struct MaskLayout {
+    size_t row_ptr, len, order, chunk, bucket, status, groups, group_off, cols;
+    int R, nchunks;
+};
+
+MaskLayout mask_layout(const sa::Layout &L)
+{
+    MaskLayout m{};
+    m.R = L.heads * L.nT;
+    m.nchunks = (m.R + sa::kMaskChunk - 1) / sa::kMaskChunk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = sa::align256(off + bytes);
+        return at;
+    };
+    m.row_ptr = take(4 * size_t(m.R + 1));
+    m.len = take(4 * size_t(m.R));
+    m.order = take(4 * size_t(m.R));
+    m.chunk = take(4 * size_t(m.nchunks) * size_t(L.nT + 1));
+    m.bucket = take(4 * size_t(L.nT + 1));
+    m.status = take(64);
+    m.groups = take(4 * 6 * size_t(L.heads) * SPARSE_ATTN_MAX_GROUPS);
+    m.group_off = take(4 * size_t(L.heads + 1));
+    m.cols = off;
+    return m;
+}
+
+long long max_pairs(const sa::Layout &L) { return (long long)L.heads * L.nT * L.nT; }
+
+struct WsLayout {
+    size_t q, k, v, o, total;
+};
+
+WsLayout ws_layout(const sparse_attn_handle *h)
+{
+    const size_t t = sa::align256(size_t(h->L.heads) * h->L.Npad * h->L.D * h->elem_bytes);
+    return WsLayout{0, t, 2 * t, 3 * t, 4 * t};
+}
+
+size_t io_bytes(const sparse_attn_handle *h)
+{
+    return size_t(h->L.heads) * h->L.N * h->L.D * h->elem_bytes;
+}
+
+int check_handle(const sparse_attn_handle *h) { return h ? SPARSE_ATTN_OK : SPARSE_ATTN_INVALID_ARG; }
+
+int check_ws(sparse_attn_handle *h, const void *ws, size_t ws_bytes)
+{
+    if (!ws)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "workspace pointer is null");
+    if (!aligned16(ws))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "workspace is not 16-byte aligned");
+    const size_t need = ws_layout(h).total;
+    if (ws_bytes < need)
+        return fail(h, SPARSE_ATTN_WORKSPACE_TOO_SMALL, "workspace holds %zu bytes, %zu needed",
+                    ws_bytes, need);
+    return SPARSE_ATTN_OK;
+}
+
+int check_io(sparse_attn_handle *h, const void *p, const char *name)
+{
+    if (!p)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "%s is null", name);
+    if (!aligned16(p))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return SPARSE_ATTN_OK;
+}
+
+sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
+{
+    const WsLayout w = ws_layout(h);
+    char *b = static_cast<char *>(ws);
+    sa::AttnParams p;
+    p.q = b + w.q;
+    p.k = b + w.k;
+    p.v = b + w.v;
+    p.o = b + w.o;
+    p.row_ptr = h->mb.row_ptr;
+    p.cols = h->mb.cols;
+    p.order = h->mb.order;
+    p.cap = h->mb.cap;
+    p.scale_log2 = h->scale * 1.4426950408889634f;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *sparse_attn_status_string(int status)
+{
+    switch (status) {
+    case SPARSE_ATTN_OK: return "ok";
+    case SPARSE_ATTN_INVALID_ARG: return "invalid argument";
+    case SPARSE_ATTN_UNSUPPORTED: return "unsupported configuration";
+    case SPARSE_ATTN_BAD_MASK: return "malformed mask";
+    case SPARSE_ATTN_WORKSPACE_TOO_SMALL: return "buffer too small";
+    case SPARSE_ATTN_NO_MASK: return "no mask set";
+    case SPARSE_ATTN_HIP_ERROR: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+const char *sparse_attn_last_error(const sparse_attn_handle *h)
+{
+    return h ? h->err.c_str() : g_create_err.c_str();
+}
+
+int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
+{
+    if (!cfg || !out)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cfg and out must be non-null");
+    *out = nullptr;
+    const sparse_attn_config &c = *cfg;
+    if (c.heads < 1)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "heads must be >= 1");
+    for (int a = 0; a < 3; ++a) {
+        if (c.grid[a] < 1 || c.tile[a] < 1)
+            return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "grid and tile sizes must be >= 1");
+    }
+    if (c.dtype != SPARSE_ATTN_F32 && c.dtype != SPARSE_ATTN_BF16)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "dtype must be F32 or BF16");
+    if (!(c.softmax_scale >= 0.f) || std::isinf(c.softmax_scale))
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "softmax_scale must be finite and >= 0");
+    if (c.head_dim != 64 && c.head_dim != 128)
+        return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "head_dim must be 64 or 128");
+    const long long B = (long long)c.tile[0] * c.tile[1] * c.tile[2];
+    if (B > 128)
+        return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "tile volume %lld exceeds 128", B);
+
+    sa::Layout L{};
+    L.T = c.grid[0];
+    L.H = c.grid[1];
+    L.W = c.grid[2];
+    // A tile larger than the grid is allowed: it is clipped like any edge
+    // tile and keeps B = tt th tw slots.
+    L.tt = c.tile[0];
+    L.th = c.tile[1];
+    L.tw = c.tile[2];
+    L.nt = (L.T + L.tt - 1) / L.tt;
+    L.ny = (L.H + L.th - 1) / L.th;
+    L.nx = (L.W + L.tw - 1) / L.tw;
+    const long long nT = (long long)L.nt * L.ny * L.nx;
+    const long long N = (long long)L.T * L.H * L.W;
+    if (nT * nT * c.heads >= (1ll << 31))
+        return fail(nullptr, SPARSE_ATTN_UNSUPPORTED,
+                    "heads * tiles^2 = %lld does not fit 32-bit index lists", nT * nT * c.heads);
+    L.nT = (int)nT;
+    L.B = (int)B;
+    L.heads = c.heads;
+    L.D = c.head_dim;
+    L.N = N;
+    L.Npad = nT * B;
+
+    auto *h = new sparse_attn_handle();
+    h->cfg = c;
+    h->L = L;
+    h->elem_bytes = c.dtype == SPARSE_ATTN_F32 ? 4 : 2;
+    h->kernel = (c.dtype == SPARSE_ATTN_BF16 && B == 128) ? SPARSE_ATTN_KERNEL_MFMA_BF16
+                                                          : SPARSE_ATTN_KERNEL_GENERIC;
+    h->scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
+    *out = h;
+    return SPARSE_ATTN_OK;
+}
+
+void sparse_attn_destroy(sparse_attn_handle *h) { delete h; }
+
+int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *info)
+{
+    if (!h || !info)
+        return SPARSE_ATTN_INVALID_ARG;
+    const WsLayout w = ws_layout(h);
+    info->tokens = h->L.N;
+    info->tiles = h->L.nT;
+    info->tile_grid[0] = h->L.nt;
+    info->tile_grid[1] = h->L.ny;
+    info->tile_grid[2] = h->L.nx;
+    info->tile_volume = h->L.B;
+    info->slots = h->L.Npad;
+    info->kernel = h->kernel;
+    info->v_layout = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? SPARSE_ATTN_LAYOUT_TILE_COLUMNS
+                                                               : SPARSE_ATTN_LAYOUT_ROWS;
+    info->ws_offset_q = w.q;
+    info->ws_offset_k = w.k;
+    info->ws_offset_v = w.v;
+    info->ws_offset_o = w.o;
+    info->ws_bytes = w.total;
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t *bytes)
+{
+    if (!h || !bytes)
+        return SPARSE_ATTN_INVALID_ARG;
+    const long long cap = (max_nnz <= 0 || max_nnz > max_pairs(h->L)) ? max_pairs(h->L) : max_nnz;
+    *bytes = mask_layout(h->L).cols + 4 * size_t(cap);
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_workspace_bytes(const sparse_attn_handle *h, size_t *bytes)
+{
+    if (!h || !bytes)
+        return SPARSE_ATTN_INVALID_ARG;
+    *bytes = ws_layout(h).total;
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void *mask_buf,
+                         size_t bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (!m || !mask_buf)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "mask and mask_buf must be non-null");
+    if (!aligned16(mask_buf))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "mask_buf is not 16-byte aligned");
+    const sa::Layout &L = h->L;
+    const MaskLayout ml = mask_layout(L);
+    const long long want = (m->max_nnz <= 0 || m->max_nnz > max_pairs(L)) ? max_pairs(L) : m->max_nnz;
+    const size_t need = ml.cols + 4 * size_t(want);
+    if (bytes < need)
+        return fail(h, SPARSE_ATTN_WORKSPACE_TOO_SMALL, "mask_buf holds %zu bytes, %zu needed", bytes,
+                    need);
+
+    std::vector<int32_t> spec;  // groups (6 ints each), then offsets (heads + 1)
+    if (m->kind == SPARSE_ATTN_MASK_BITMAP) {
+        if (!m->bitmap)
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "bitmap mask without a bitmap pointer");
+    } else if (m->kind == SPARSE_ATTN_MASK_DUAL_WINDOW) {
+        if (!m->groups || !m->groups_per_head)
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "dual-window mask without groups");
+        std::vector<int32_t> off(L.heads + 1, 0);
+        for (int hh = 0; hh < L.heads; ++hh) {
+            const int ng = m->groups_per_head[hh];
+            if (ng < 1 || ng > SPARSE_ATTN_MAX_GROUPS)
+                return fail(h, SPARSE_ATTN_BAD_MASK, "head %d has %d groups (1..%d allowed)", hh, ng,
+                            SPARSE_ATTN_MAX_GROUPS);
+            off[hh + 1] = off[hh] + ng;
+        }
+        for (int hh = 0; hh < L.heads; ++hh) {
+            long long prev_hi = -1;
+            for (int g = off[hh]; g < off[hh + 1]; ++g) {
+                const sparse_attn_window_group &G = m->groups[g];
+                const bool last = g + 1 == off[hh + 1];
+                if (G.dt_lo < 0 || (G.dt_hi < 0 && G.dt_hi != -1) ||
+                    (G.dt_hi >= 0 && G.dt_hi < G.dt_lo))
+                    return fail(h, SPARSE_ATTN_BAD_MASK, "head %d group %d: bad distance range [%d, %d]",
+                                hh, g - off[hh], G.dt_lo, G.dt_hi);
+                if (G.dt_hi == -1 && !last)
+                    return fail(h, SPARSE_ATTN_BAD_MASK,
+                                "head %d group %d: an unbounded group must be the last", hh, g - off[hh]);
+                if (G.dt_lo <= prev_hi)
+                    return fail(h, SPARSE_ATTN_BAD_MASK,
+                                "head %d group %d: groups must be sorted and disjoint", hh, g - off[hh]);
+                for (int w = 0; w < 2; ++w) {
+                    if (G.ry[w] < -1 || G.rx[w] < -1)
+                        return fail(h, SPARSE_ATTN_BAD_MASK,
+                                    "head %d group %d window %d: half-extents must be >= -1", hh,
+                                    g - off[hh], w);
+                }
+                prev_hi = G.dt_hi;
+                spec.insert(spec.end(), {G.dt_lo, G.dt_hi, G.ry[0], G.ry[1], G.rx[0], G.rx[1]});
+            }
+        }
+        spec.insert(spec.end(), off.begin(), off.end());
+    } else {
+        return fail(h, SPARSE_ATTN_BAD_MASK, "unknown mask kind %d", m->kind);
+    }
+
+    char *base = static_cast<char *>(mask_buf);
+    sa::MaskBuffers mb{};
+    mb.row_ptr = reinterpret_cast<int *>(base + ml.row_ptr);
+    mb.len = reinterpret_cast<int *>(base + ml.len);
+    mb.order = reinterpret_cast<int *>(base + ml.order);
+    mb.chunk = reinterpret_cast<int *>(base + ml.chunk);
+    mb.bucket = reinterpret_cast<int *>(base + ml.bucket);
+    mb.status = reinterpret_cast<int *>(base + ml.status);
+    mb.groups = reinterpret_cast<int *>(base + ml.groups);
+    mb.group_off = reinterpret_cast<int *>(base + ml.group_off);
+    mb.cols = reinterpret_cast<int *>(base + ml.cols);
+    mb.cap = std::min<long long>((bytes - ml.cols) / 4, max_pairs(L));
+    mb.R = ml.R;
+    mb.nchunks = ml.nchunks;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    h->has_mask = false;
+    if (m->kind == SPARSE_ATTN_MASK_DUAL_WINDOW) {
+        h->spec = std::move(spec);
+        const size_t ngroups = (h->spec.size() - (L.heads + 1)) / 6;
+        hipError_t e = hipMemcpyAsync(mb.groups, h->spec.data(), ngroups * 6 * 4,
+                                      hipMemcpyHostToDevice, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(mb.group_off, h->spec.data() + ngroups * 6, (L.heads + 1) * 4,
+                               hipMemcpyHostToDevice, s);
+        if (e != hipSuccess)
+            return hip_fail(h, e, "uploading the window spec");
+    }
+    const hipError_t e = sa::launch_compile_mask(
+        L, m->kind == SPARSE_ATTN_MASK_BITMAP ? 0 : 1, m->bitmap, mb, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "mask compile launch");
+    h->mb = mb;
+    h->has_mask = true;
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_permute_inputs(sparse_attn_handle *h, const void *q, const void *k, const void *v,
+                               void *ws, size_t ws_bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, q, "q")) || (st = check_io(h, k, "k")) || (st = check_io(h, v, "v")) ||
+        (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    const size_t n = io_bytes(h);
+    const WsLayout w = ws_layout(h);
+    for (const void *p : {q, k, v})
+        if (overlaps(p, n, ws, w.total))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "inputs must not overlap the workspace");
+    char *b = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_permute_rows(h->L, h->elem_bytes, q, b + w.q, s);
+    if (e == hipSuccess)
+        e = sa::launch_permute_rows(h->L, h->elem_bytes, k, b + w.k, s);
+    if (e == hipSuccess)
+        e = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16
+                ? sa::launch_permute_tile_columns(h->L, v, b + w.v, s)
+                : sa::launch_permute_rows(h->L, h->elem_bytes, v, b + w.v, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "permute launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_attend(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_ws(h, ws, ws_bytes)))
+        return st;
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before attention");
+    const sa::AttnParams p = attn_params(h, ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16
+                             ? sa::launch_attention_mfma(h->L, p, s)
+                             : sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "attention launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *o,
+                                 void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, o, "o")) || (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    const WsLayout w = ws_layout(h);
+    if (overlaps(o, io_bytes(h), ws, w.total))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "o must not overlap the workspace");
+    const hipError_t e = sa::launch_unpermute_rows(h->L, h->elem_bytes, static_cast<char *>(ws) + w.o,
+                                                   o, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(h, e, "unpermute launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
+                        void *ws, size_t ws_bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, q, "q")) || (st = check_io(h, k, "k")) || (st = check_io(h, v, "v")) ||
+        (st = check_io(h, o, "o")) || (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before forward");
+    const size_t n = io_bytes(h);
+    for (const void *p : {q, k, v})
+        if (overlaps(o, n, p, n))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "o must not overlap q, k or v");
+    if ((st = sparse_attn_permute_inputs(h, q, k, v, ws, ws_bytes, stream)))
+        return st;
+    if ((st = sparse_attn_attend(h, ws, ws_bytes, stream)))
+        return st;
+    return sparse_attn_unpermute_output(h, ws, ws_bytes, o, stream);
+}
+
+int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32_t layout,
+                        void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, src, "src")) || (st = check_io(h, dst, "dst")))
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (layout == SPARSE_ATTN_LAYOUT_ROWS) {
+        e = sa::launch_permute_rows(h->L, h->elem_bytes, src, dst, s);
+    } else if (layout == SPARSE_ATTN_LAYOUT_TILE_COLUMNS) {
+        if (h->elem_bytes != 2 || h->L.B % 8 != 0)
+            return fail(h, SPARSE_ATTN_UNSUPPORTED,
+                        "tile-column layout needs bf16 and a tile volume divisible by 8");
+        e = sa::launch_permute_tile_columns(h->L, src, dst, s);
+    } else {
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "unknown layout %d", layout);
+    }
+    if (e != hipSuccess)
+        return hip_fail(h, e, "permute launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_unpermute(sparse_attn_handle *h, const void *src, void *dst, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, src, "src")) || (st = check_io(h, dst, "dst")))
+        return st;
+    const hipError_t e =
+        sa::launch_unpermute_rows(h->L, h->elem_bytes, src, dst, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(h, e, "unpermute launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_read_index_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t *cols,
+                                 int64_t cols_capacity, int32_t *order, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (!row_ptr || !order || (!cols && cols_capacity > 0) || cols_capacity < 0)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "null destination");
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "no mask set");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int R = h->mb.R;
+    hipError_t e = hipMemcpyAsync(row_ptr, h->mb.row_ptr, 4 * size_t(R + 1), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(order, h->mb.order, 4 * size_t(R), hipMemcpyDeviceToDevice, s);
+    const long long n = std::min<long long>(cols_capacity, h->mb.cap);
+    if (e == hipSuccess && n > 0)
+        e = hipMemcpyAsync(cols, h->mb.cols, 4 * size_t(n), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "copying index lists");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (!nnz || !overflow)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "null output");
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "no mask set");
+    int32_t st[2];
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(st, h->mb.status, sizeof st, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "reading mask status");
+    *nnz = st[0];
+    *overflow = st[1];
+    return SPARSE_ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+/*
+ * sparse_attn.h - block-sparse (tile-masked) attention forward over a 3D
+ * video token grid, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  Video diffusion transformers attend over a latent grid of
+ * T x H x W tokens.  The grid is cut into tiles of tt x th x tw tokens and
+ * every head h carries its own binary mask M_h over pairs of tiles: query
+ * tile i attends to key tile j only when M_h[i, j] is set (Compact Attention
+ * page, abstract: head-specific masks in one tile-aligned family; Fig. 1
+ * caption: retained query-key regions; Fig. 3 caption: online inference loads
+ * precomputed masks into block-sparse attention kernels and reuses each one
+ * over an interval of adjacent denoising steps).  Inside the kept set the
+ * result is exact softmax attention over the original keys and values (SCOPE
+ * review page, abstract), with scores scaled by 1/sqrt(head_dim) by default:
+ *
+ *     O[h, n] = sum_{m kept} softmax_m(s q_n . k_m) v_m,   0 if nothing is kept.
+ *
+ * Masks come either as a dense tile bitmap or as dual-window specs: per head,
+ * temporal-distance groups, each with two rectangular windows of tiles around
+ * the query tile (Compact Attention page, Fig. 1 caption part (3); Fig. 4
+ * caption).  The pages give no formula for the windows; the reading
+ * implemented here is stated at sparse_attn_window_group.
+ *
+ * Calling pattern (mirrors the pages' offline/online split):
+ *     sparse_attn_create        once per shape (host only)
+ *     sparse_attn_set_mask      once per mask; compiles it on the GPU
+ *     sparse_attn_forward       many times; permute -> attend -> unpermute
+ *     sparse_attn_destroy
+ *
+ * Conventions shared by every entry point:
+ *   - Every call returns a status (SPARSE_ATTN_OK = 0).  All argument checks
+ *     finish before anything is enqueued, so a failed call leaves no GPU work
+ *     behind.  sparse_attn_last_error() then describes the failure.
+ *   - Device pointers are caller-owned HIP device memory (for example torch
+ *     tensors), 16-byte aligned.  The library never allocates device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *     work and return without synchronizing, unless stated otherwise.
+ *     Asynchronous faults surface at the caller's next synchronization.
+ *   - A handle may not be used by two host threads at once; separate handles
+ *     are independent.
+ *   - There is no batch dimension: fold batch into heads when grids match.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    SPARSE_ATTN_OK = 0,
+    SPARSE_ATTN_INVALID_ARG = 1,         /* null/misaligned/aliased pointer, bad value */
+    SPARSE_ATTN_UNSUPPORTED = 2,         /* valid but outside what the library handles */
+    SPARSE_ATTN_BAD_MASK = 3,            /* malformed mask description */
+    SPARSE_ATTN_WORKSPACE_TOO_SMALL = 4, /* a caller buffer is smaller than required */
+    SPARSE_ATTN_NO_MASK = 5,             /* forward/attend before set_mask */
+    SPARSE_ATTN_HIP_ERROR = 6            /* the HIP runtime reported an error */
+};
+
+/* Element types of Q, K, V and O. */
+enum { SPARSE_ATTN_F32 = 0, SPARSE_ATTN_BF16 = 1 };
+
+/* Mask kinds. */
+enum { SPARSE_ATTN_MASK_BITMAP = 0, SPARSE_ATTN_MASK_DUAL_WINDOW = 1 };
+
+/* Layouts of a permuted tensor (sparse_attn_permute). */
+enum {
+    /* [heads][nT * B][head_dim]: slot-major rows, one row per slot. */
+    SPARSE_ATTN_LAYOUT_ROWS = 0,
+    /* [heads][nT][head_dim][B]: per tile, one row of B slots per feature
+     * (the transposed value tile the MFMA kernel reads). */
+    SPARSE_ATTN_LAYOUT_TILE_COLUMNS = 1
+};
+
+/* Attention kernels forward may select (sparse_attn_layout_info.kernel). */
+enum {
+    SPARSE_ATTN_KERNEL_MFMA_BF16 = 0, /* bf16 matrix-core kernel: B = 128, head_dim 64 or 128 */
+    SPARSE_ATTN_KERNEL_GENERIC = 1    /* fp32 vector-ALU kernel: any supported shape */
+};
+
+/* Maximum temporal-distance groups per head in a dual-window mask. */
+#define SPARSE_ATTN_MAX_GROUPS 8
+
+typedef struct sparse_attn_config {
+    int32_t heads;         /* >= 1 */
+    int32_t head_dim;      /* 64 or 128 */
+    int32_t grid[3];       /* T, H, W: latent token grid, each >= 1 */
+    int32_t tile[3];       /* tt, th, tw: tile shape, each >= 1, product B <= 128 */
+    int32_t dtype;         /* SPARSE_ATTN_F32 or SPARSE_ATTN_BF16 */
+    float softmax_scale;   /* score scale s; 0 selects 1 / sqrt(head_dim) */
+} sparse_attn_config;
+
+/*
+ * One temporal-distance group of a dual-window mask (Compact Attention
+ * page, Fig. 1 caption part (3); Fig. 4 caption).  Tiles are located by
+ * (a, b, e) = tile coordinates along (t, y, x).  A query tile i keeps key
+ * tile j when |a_i - a_j| lies in [dt_lo, dt_hi] (dt_hi = -1: no upper
+ * bound) and, for some w in {0, 1} with ry[w] >= 0 and rx[w] >= 0,
+ * |b_i - b_j| <= ry[w] and |e_i - e_j| <= rx[w].  Windows are centred on the
+ * query tile and clip at the grid edge; a half-extent of -1 disables the
+ * window.  The groups of one head must be sorted, disjoint and satisfy
+ * 0 <= dt_lo <= dt_hi (or dt_hi = -1 for the last group only).
+ */
+typedef struct sparse_attn_window_group {
+    int32_t dt_lo, dt_hi;
+    int32_t ry[2];
+    int32_t rx[2];
+} sparse_attn_window_group;
+
+typedef struct sparse_attn_mask {
+    int32_t kind; /* SPARSE_ATTN_MASK_BITMAP or SPARSE_ATTN_MASK_DUAL_WINDOW */
+    /* BITMAP: device uint8 [heads][nT][nT], row-major (h, i, j); nonzero keeps
+     * key tile j for query tile i.  Read during set_mask only. */
+    const uint8_t *bitmap;
+    /* DUAL_WINDOW: host arrays, copied during set_mask.  groups holds the
+     * groups of head 0, then head 1, ...; groups_per_head[h] in 1..MAX_GROUPS. */
+    const sparse_attn_window_group *groups;
+    const int32_t *groups_per_head;
+    /* Upper bound on kept tile pairs over all heads, sizing the index list;
+     * <= 0 means heads * nT * nT. */
+    int64_t max_nnz;
+} sparse_attn_mask;
+
+typedef struct sparse_attn_layout_info {
+    int64_t tokens;        /* N = T * H * W */
+    int64_t tiles;         /* nT = nt * ny * nx */
+    int32_t tile_grid[3];  /* nt, ny, nx = ceil(T / tt), ceil(H / th), ceil(W / tw) */
+    int32_t tile_volume;   /* B = tt * th * tw: slots per tile */
+    int64_t slots;         /* N_pad = nT * B */
+    int32_t kernel;        /* SPARSE_ATTN_KERNEL_* that forward runs */
+    int32_t v_layout;      /* SPARSE_ATTN_LAYOUT_* of the permuted V in the workspace */
+    /* Byte offsets of the permuted Q, K, V and of the tile-major output O
+     * inside the forward workspace, and the workspace size. */
+    size_t ws_offset_q, ws_offset_k, ws_offset_v, ws_offset_o, ws_bytes;
+} sparse_attn_layout_info;
+
+typedef struct sparse_attn_handle sparse_attn_handle;
+
+/*
+ * Validate a configuration and plan the tile layout (host only, no device
+ * call).  Tiles are numbered raster over the tile grid (t, then y, then x);
+ * tiles at the far edges of a grid the tile does not divide are clipped.
+ * Each tile owns B consecutive slots: its c real tokens fill the first c in
+ * raster order over the clipped tile, the rest are empty.
+ * Errors: INVALID_ARG (null, non-positive sizes, bad dtype),
+ * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31).
+ * On success *out owns host memory only; release it with sparse_attn_destroy.
+ */
+int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out);
+
+/* Release a handle (host memory only).  NULL is a no-op. */
+void sparse_attn_destroy(sparse_attn_handle *h);
+
+/* Describe the planned layout and workspace.  Errors: INVALID_ARG. */
+int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *info);
+
+/* Device bytes the compiled-mask buffer needs for at most max_nnz kept tile
+ * pairs (<= 0: heads * nT * nT).  Errors: INVALID_ARG. */
+int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t *bytes);
+
+/* Device bytes of the forward workspace (permuted Q, K, V and O).
+ * Errors: INVALID_ARG. */
+int sparse_attn_workspace_bytes(const sparse_attn_handle *h, size_t *bytes);
+
+/*
+ * Compile a mask on the GPU into mask_buf: per query-tile row r = h nT + i
+ * the kept key tiles in ascending order (row offsets by exclusive sum of row
+ * lengths), and a work order of rows by decreasing length, ties by row id.
+ * mask_buf (device, caller-owned, at least sparse_attn_mask_bytes(max_nnz)
+ * bytes) must stay alive and unmodified while forwards use the mask; calling
+ * again replaces the mask.  If the mask keeps more pairs than max_nnz, the
+ * index list is truncated (never overrun), forward uses the truncated lists,
+ * and sparse_attn_mask_info reports the overflow.
+ * Errors: INVALID_ARG (null pointers), BAD_MASK (kind, group count, order or
+ * extents), WORKSPACE_TOO_SMALL (bytes), HIP_ERROR.
+ */
+int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void *mask_buf,
+                         size_t bytes, void *stream);
+
+/*
+ * Block-sparse attention forward.  q, k, v, o: device [heads][T*H*W][head_dim]
+ * in raster token order, element type cfg.dtype; o must not overlap q, k, v
+ * or ws.  ws: device workspace of at least sparse_attn_workspace_bytes.
+ * Enqueues permute (Q, K, V to tile-major) -> attention over the kept tile
+ * pairs -> unpermute (O back to raster order).
+ * Errors: INVALID_ARG, NO_MASK, WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* The three stages of sparse_attn_forward, callable one by one (same
+ * arguments and errors); forward is exactly these in order. */
+int sparse_attn_permute_inputs(sparse_attn_handle *h, const void *q, const void *k, const void *v,
+                               void *ws, size_t ws_bytes, void *stream);
+int sparse_attn_attend(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *stream);
+int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *o,
+                                 void *stream);
+
+/*
+ * Test hooks.
+ * sparse_attn_permute: src [heads][N][head_dim] raster -> dst in `layout`
+ *   (SPARSE_ATTN_LAYOUT_*), empty slots zero.  dst holds heads * nT * B *
+ *   head_dim elements.
+ * sparse_attn_unpermute: src [heads][nT * B][head_dim] rows -> dst
+ *   [heads][N][head_dim] raster; empty slots are not read.
+ * sparse_attn_read_index_lists: copy the compiled row offsets (int32
+ *   [heads nT + 1]), index list (int32, first min(nnz, cols_capacity)
+ *   entries) and work order (int32 [heads nT]) into device buffers.
+ * sparse_attn_mask_info: synchronizes `stream`, then reports the number of
+ *   kept pairs and whether the index list overflowed its capacity.
+ * Errors: INVALID_ARG, NO_MASK (index lists), HIP_ERROR.
+ */
+int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32_t layout,
+                        void *stream);
+int sparse_attn_unpermute(sparse_attn_handle *h, const void *src, void *dst, void *stream);
+int sparse_attn_read_index_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t *cols,
+                                 int64_t cols_capacity, int32_t *order, void *stream);
+int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow, void *stream);
+
+/* Static description of a status code. */
+const char *sparse_attn_status_string(int status);
+
+/* Message of the last failed call on this handle ("" if none).  The string
+ * stays valid until the next call on the handle.  NULL handle: the message of
+ * the last failed sparse_attn_create on this thread. */
+const char *sparse_attn_last_error(const sparse_attn_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -34,6 +34,8 @@ This module holds the input recipes only.  Counting formulas used to steer
 the recipes towards their density targets live in ``accounting``.
 """
 
+import concurrent.futures
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -121,11 +123,23 @@ def _encode(x, dtype):
     return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
+def _per_head(heads, fn):
+    """Run fn(h) for every head on a thread pool (numpy releases the GIL in
+    the RNG and array kernels); each head has its own seeded stream, so the
+    result does not depend on scheduling."""
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), heads))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fn, range(heads)))
+
+
 def _gaussian(cfg, stream, heads):
     N, d = cfg.tokens, cfg.head_dim
     out = np.empty((heads, N, d), dtype=np.float32 if cfg.dtype == "f32" else np.uint16)
-    for h in range(heads):
+
+    def one(h):
         out[h] = _encode(_rng(cfg, stream, h).standard_normal((N, d), dtype=np.float32), cfg.dtype)
+
+    _per_head(heads, one)
     return out
 
 
@@ -311,27 +325,35 @@ def _wan_qk(cfg, stream, heads):
     ang = p @ omega.T
     phi = (np.concatenate([np.cos(ang), np.sin(ang)], axis=1) / np.sqrt(8.0)).astype(np.float32)
     out = np.empty((heads, cfg.tokens, d), dtype=np.uint16)
-    for h in range(heads):
+
+    def one(h):
         u, _ = np.linalg.qr(_rng(cfg, 4, h + 1).standard_normal((d, 16)))
         bias = phi @ u.T.astype(np.float32)
         z = _rng(cfg, stream, h).standard_normal((cfg.tokens, d), dtype=np.float32)
         out[h] = _encode(np.float32(alpha) * (z + np.float32(beta) * bias), cfg.dtype)
+
+    _per_head(heads, one)
     return out
 
 
-def make_workload(name, heads=None):
+def make_workload(name, heads=None, masks_only=False):
     """Build the named workload; ``heads`` limits generation to the first
-    heads (identical to those heads of the full workload)."""
+    heads (identical to those heads of the full workload).  ``masks_only``
+    skips drawing Q/K/V when the mask recipe does not need them (q, k, v are
+    then None)."""
     cfg = CONFIGS[name]
     heads = cfg.heads if heads is None else int(heads)
     if not 1 <= heads <= cfg.heads:
         raise ValueError(f"heads must be in 1..{cfg.heads}")
     info = {}
-    if cfg.mask == "wan_windows":
+    if masks_only and cfg.mask != "hunyuan_topk":
+        q = k = v = None
+    elif cfg.mask == "wan_windows":
         q, k = _wan_qk(cfg, 0, heads), _wan_qk(cfg, 1, heads)
+        v = _gaussian(cfg, 2, heads)
     else:
         q, k = _gaussian(cfg, 0, heads), _gaussian(cfg, 1, heads)
-    v = _gaussian(cfg, 2, heads)
+        v = None if masks_only else _gaussian(cfg, 2, heads)
 
     if cfg.mask == "bernoulli":
         wl = Workload(cfg, heads, q, k, v, "bitmap", bitmap=_bernoulli_bitmap(cfg, heads))
