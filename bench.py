@@ -1,0 +1,254 @@
+"""Benchmark: block-sparse attention forward on one MI355X.
+
+One step is one pass of the whole hot path over the Wan2.1-shaped 720p
+workload (40 heads, head_dim 128, bf16, grid 21x45x80 = 75,600 tokens, tile
+1x8x16, local / axial / near-dense dual-window masks at ~26% tile density):
+mask compile -> permute Q/K/V to tile-major -> block-sparse attention ->
+unpermute O.  Inputs are synthetic and resident in HBM before timing.
+
+Printed: one JSON line.  `value` is the effective throughput of the whole
+step, F_alg / step time, where F_alg = 4 d sum over kept tile pairs of
+c_i c_j (real tokens only).  `roofline` reports the attention kernel alone
+against the bf16 dense matrix peak; `attention.dense_speedup` is the same
+kernel's time with an all-ones mask divided by its time with the real mask.
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the same
+workload (rank 0, N = 1 only).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan]
+                       [--no-cpu-baseline] [--copy-calibration]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 FLOP/clk x 2.4 GHz, dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "block-sparse attn fwd effective TFLOP/s + % MFMA peak; speedup vs dense mask"
+WORKLOAD_NAMES = {
+    "wan": "wan2.1-shaped 720p: 40 heads x 75,600 tokens, d=128, tile 1x8x16, dual-window masks",
+    "hunyuan": "hunyuanvideo-shaped 720p: 24 heads x 118,800 tokens, d=128, tile 1x8x16, top-k tile masks",
+    "long": "long-video stress: 40 heads x 151,200 tokens, d=128, tile 1x8x16, +-4 frame axial masks",
+    "small": "small video: 12 heads x 9,600 tokens, d=128, tile 1x8x16, dual-window masks",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_wan_traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_major_amd", "csrc", "attn_mfma.hip")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_per_launch(workload):
+    """HBM bytes per attention launch from committed counter runs, or None if
+    they were taken on another version of the kernel or workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, M, budget_s=15.0):
+    """Time the fp64 oracle on sampled query rows of the workload."""
+    import oracle
+
+    threads = oracle.default_threads()
+    N, d = wl.config.tokens, wl.head_dim
+    counts = oracle.tile_counts(wl.grid, wl.tile).astype(np.float64)
+    _, pos = oracle.perm(wl.grid, wl.tile)
+    tile_of = pos // int(np.prod(wl.tile))
+    keys_per_row = np.stack([M[h].astype(np.float64) @ counts for h in range(wl.heads)])  # [heads, nT]
+    rng = np.random.default_rng(12345)
+
+    def rows_flops(n):
+        rows = rng.choice(wl.heads * N, size=n, replace=False)
+        f = 4.0 * d * keys_per_row[rows // N, tile_of[rows % N]].sum()
+        return np.sort(rows).astype(np.int64), f
+
+    rows, f = rows_flops(max(64, threads * 8))  # calibration
+    t0 = time.perf_counter()
+    oracle.attention_rows(wl.grid, wl.tile, wl.q, wl.k, wl.v, M, rows, threads=threads)
+    rate = f / (time.perf_counter() - t0)
+    n = int(min(wl.heads * N, max(64, budget_s * rate / (f / len(rows)))))
+    rows, f = rows_flops(n)
+    t0 = time.perf_counter()
+    oracle.attention_rows(wl.grid, wl.tile, wl.q, wl.k, wl.v, M, rows, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} query rows drawn uniformly over all heads and tokens of the workload "
+                      f"({f / 1e12:.3f} TFLOP algorithmic, {dt:.1f} s wall, fp64, OpenMP)",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB device copy (counter calibration runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(heads are independent, so a multi-GPU run would shard heads with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_major_amd as sa
+    from workloads import make_workload, ones_bitmap
+
+    torch.cuda.set_device(0)
+    wl = make_workload(args.workload)
+    cfg = wl.config
+    info = wl.info
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+    q, k, v = t(wl.q), t(wl.k), t(wl.v)
+    o = torch.empty_like(q)
+    h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, wl.dtype)
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    mask_buf = torch.empty(sa.sparse_attn_mask_bytes(h, info["nnz"]), dtype=torch.uint8, device="cuda")
+    dense_buf = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+    ones = t(ones_bitmap(wl))
+    stream = torch.cuda.current_stream()
+
+    def set_mask():
+        if wl.mask_kind == "bitmap":
+            sa.sparse_attn_set_mask(h, mask_buf, bitmap=t(wl.bitmap), max_nnz=info["nnz"])
+        else:
+            sa.sparse_attn_set_mask(h, mask_buf, groups=wl.groups, groups_per_head=wl.groups_per_head,
+                                    max_nnz=info["nnz"])
+
+    if wl.mask_kind == "bitmap":
+        bitmap_dev = t(wl.bitmap)
+
+        def set_mask():  # noqa: F811  (bitmap already resident)
+            sa.sparse_attn_set_mask(h, mask_buf, bitmap=bitmap_dev, max_nnz=info["nnz"])
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(ev=None):
+        if ev is None:
+            set_mask()
+            sa.sparse_attn_forward(h, q, k, v, o, ws)
+            return
+        ev[0].record(stream)
+        set_mask()
+        ev[1].record(stream)
+        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        ev[2].record(stream)
+        sa.sparse_attn_attend(h, ws)
+        ev[3].record(stream)
+        sa.sparse_attn_unpermute_output(h, ws, o)
+        ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[E() for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events])  # ms
+    mask_ms, perm_ms, attn_ms, unperm_ms = st.mean(axis=0)
+    attn_min = st[:, 2].min()
+    nnz, overflow = sa.sparse_attn_mask_info(h)
+    assert nnz == info["nnz"] and not overflow, (nnz, info["nnz"], overflow)
+
+    # Same kernel, same inputs, all-ones mask.
+    dense_ms = None
+    if not args.no_dense:
+        sa.sparse_attn_set_mask(h, dense_buf, bitmap=ones)
+        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        for _ in range(2):
+            sa.sparse_attn_attend(h, ws)
+        dense = []
+        for _ in range(max(3, args.steps // 4)):
+            a, b = E(), E()
+            a.record(stream)
+            sa.sparse_attn_attend(h, ws)
+            b.record(stream)
+            dense.append((a, b))
+        torch.cuda.synchronize()
+        dense_ms = float(np.mean([a.elapsed_time(b) for a, b in dense]))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    F = info["flops_alg"]
+    N, d, heads = cfg.tokens, cfg.head_dim, wl.heads
+    elem = 2
+    attn_tflops = F / (attn_ms * 1e-3) / 1e12
+    in_bytes = heads * N * d * elem
+    slot_bytes = heads * info["nT"] * info["tile_volume"] * d * elem
+    perm_bytes = 3 * (in_bytes + slot_bytes)
+    unperm_bytes = 2 * in_bytes  # real rows read, raster rows written
+    traffic = traffic_per_launch(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": F / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "heads": heads, "head_dim": d,
+                   "grid": list(cfg.grid), "tile": list(cfg.tile), "tokens": N,
+                   "tile_density": round(info["tile_density"], 5),
+                   "token_density": round(info["token_density"], 5),
+                   "step": "mask compile + permute + block-sparse attention + unpermute"},
+        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel<128>", "achieved": attn_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "flops_per_launch": F},
+        "attention": {"ms": attn_ms, "ms_min": float(attn_min), "tflops": attn_tflops,
+                      "pct_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS,
+                      "tflops_issued": info["flops_issued"] / (attn_ms * 1e-3) / 1e12,
+                      "dense_ms": dense_ms,
+                      "dense_speedup": dense_ms / attn_ms if dense_ms else None,
+                      "ideal_speedup": info["flops_dense"] / F,
+                      "dense_tflops": info["flops_dense"] / (dense_ms * 1e-3) / 1e12 if dense_ms else None},
+        "stages_ms": {"mask_compile": mask_ms, "permute_qkv": perm_ms, "attention": attn_ms,
+                      "unpermute_o": unperm_ms},
+        "stages_gbs": {"permute_qkv": perm_bytes / (perm_ms * 1e-3) / 1e9,
+                       "unpermute_o": unperm_bytes / (unperm_ms * 1e-3) / 1e9,
+                       "peak": PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        M = oracle.mask_of(wl)
+        result["cpu_baseline"] = cpu_baseline(wl, M)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -52,6 +52,28 @@ __host__ __device__ inline int tile_real_count(const Layout &L, int tau)
     return r.et * r.ey * r.ex;
 }
 
+// Division of 0 <= n < 2^31 by a fixed divisor 1 <= d < 2^31 with one
+// multiply-high, add and shift: the round-up method of Granlund and
+// Montgomery, "Division by invariant integers using multiplication" (1994):
+// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1, q = (mulhi(n, m) + n) >> s.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((1ull << s) < d)
+        ++s;
+    const uint64_t m = ((1ull << 32) * ((1ull << s) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, s};
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f)
+{
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
 // Round a byte count up to a 256-byte boundary.
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -98,6 +120,9 @@ struct AttnParams {
     const int *order;
     long long cap;      // valid entries of cols
     float scale_log2;   // softmax scale * log2(e)
+    int xcd_chunk;      // rows per XCD chunk of the work order (0: plain order)
+    FastDiv div_plane;  // ny * nx: tiles per tile-grid plane
+    FastDiv div_row;    // nx: tiles per tile-grid row
 };
 
 // bf16 matrix-core kernel: B == 128, D in {64, 128}.
