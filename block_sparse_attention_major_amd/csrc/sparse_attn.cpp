@@ -142,8 +142,9 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     p.order = h->mb.order;
     p.cap = h->mb.cap;
     p.scale_log2 = h->scale * 1.4426950408889634f;
-    const char *env = getenv("SPARSE_ATTN_XCD_CHUNK");
-    p.xcd_chunk = env ? atoi(env) : 32;
+    // Consecutive work items of one XCD take 32 consecutive (longest-first)
+    // rows, so query tiles that share key tiles share that XCD's L2.
+    p.xcd_chunk = 32;
     p.div_plane = sa::make_fastdiv(uint32_t(h->L.ny) * uint32_t(h->L.nx));
     p.div_row = sa::make_fastdiv(uint32_t(h->L.nx));
     return p;
