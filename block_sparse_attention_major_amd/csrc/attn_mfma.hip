@@ -8,18 +8,26 @@
 // original keys and values).  Dropped tile pairs cost no loads and no FLOPs.
 //
 // Design (ours, for CDNA4; the pages give no kernel design):
-//  - One workgroup of 4 waves per (head, query tile); tile = 128 slots, each
-//    wave owns 32 query slots.  Two workgroups share a CU, so each SIMD runs
-//    two independent waves and overlaps one's softmax with the other's MFMAs.
-//    Workgroups follow the compiled longest-first order, remapped so each XCD
-//    (which owns its L2) takes contiguous chunks of it: neighbouring rows
-//    share key tiles.
-//  - Keys are consumed in stages of 64 (half a tile).  K and the transposed V
-//    tile of a stage are copied global -> LDS by the DMA path
+//  - One workgroup of 8 waves per pair of query tiles of one head (tiles
+//    next to each other along y, t or x; see pair_tiles), one workgroup per
+//    CU.  Waves 0-3 (group A) serve the first tile, waves 4-7 (group B) the
+//    second, 32 query slots per wave.  Both walk the union of the two key
+//    lists, so a key tile kept by both is loaded once for 256 queries; each
+//    list entry says which of the two keeps it, and a group skips the math
+//    of entries its tile does not keep.
+//  - Ping-pong: each SIMD hosts one wave of each group, and B runs half a
+//    step behind A, so in every phase one of the two issues matrix products
+//    while the other runs its exponentials (schedule in the kernel body).
+//  - Keys are consumed in stages of 64 (half a key tile).  K and the
+//    transposed V tile of a stage are copied global -> LDS by the DMA path
 //    (global_load_lds_dwordx4: no registers, no LDS store instructions) into
-//    one of two statically addressed buffers, one stage ahead of the math.
-//    The empty tail of a clipped key tile (80 of 128 slots at 720p) is
-//    skipped at 32-key granularity.
+//    a ring of four statically addressed slots, two stages ahead of the
+//    math, the copies interleaved with the matrix products.  The empty tail
+//    of a clipped key tile (80 of 128 slots at 720p) is skipped at 32-key
+//    granularity.
+//  - Workgroups follow the compiled longest-first order of the pair lists,
+//    remapped so each XCD (which owns its L2) takes contiguous chunks of it:
+//    neighbouring pairs share key tiles.
 //  - Scores are computed transposed, S^T = K Q^T, so each lane holds 16 keys
 //    of one query: row max and row sum are in-lane, plus one exchange with
 //    the lane 32 apart (v_permlane32_swap).  K rows are fed to the MFMA in a
@@ -27,7 +35,8 @@
 //    order of the next product, O^T += V^T P^T, whose accumulator again keeps
 //    one query per lane (the rescale is in-lane).
 //  - V arrives pre-transposed per tile ([D][128], written by the permute
-//    stage), so V^T operand reads are plain 16-byte LDS reads.
+//    stage), so V^T operand reads are plain 16-byte LDS reads, issued one
+//    k-step ahead of the products that use them.
 //  - LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
 //    16 distinct chunk positions per 16 lanes.
 //  - Online softmax in fp32 and exp2 with a lazily moved running max; row
@@ -43,10 +52,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;    // waves 0-3: first query tile of the pair, 4-7: second
+constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 128;   // slots per tile
 constexpr int kStage = 64;   // keys per LDS stage
-constexpr int kList = 2048;  // key-tile ids staged in LDS at a time
+constexpr int kList = 2048;  // pair-list entries staged in LDS at a time
 
 // Probabilities are kept below 2^kLazy (see the online softmax below).
 constexpr float kLazy = 8.0f;
@@ -107,42 +117,70 @@ __device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P,
     return min(L.tt, L.T - a * L.tt) * min(L.th, L.H - b * L.th) * min(L.tw, L.W - e * L.tw);
 }
 
-// One stage (64 keys, half `half` of key tile j) in LDS: K rows [64][D] then
-// transposed V [D][64], both swizzled.  The stage is 2 * D KB, moved as 1 KB
-// DMA blocks of 64 lanes x 16 bytes; LDS byte 16 l of a block receives lane
-// l's load, so each lane fetches the global chunk that the swizzle puts
-// there.  Wave w issues blocks [w * BPW, (w + 1) * BPW).
+// Geometry of one stage (64 keys of one key tile) in LDS: K rows [64][D] and
+// transposed V [D][64], each swizzled and D KB, moved as 1 KB DMA blocks of
+// 64 lanes x 16 bytes.  Wave w moves blocks [w BPW, (w + 1) BPW) of the 2 D
+// blocks: the first half of the waves moves K, the second half V^T.
 template <int D>
-__device__ __forceinline__ void issue_stage(lds_char *stage, const uint16_t *__restrict__ Kp,
-                                            const uint16_t *__restrict__ Vt, const Layout &L, int h,
-                                            int j, int half, int wave, int lane)
+struct Stage {
+    static constexpr int RCK = D / 8;                   // 16-byte chunks per K row
+    static constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks (V^T has as many)
+    static constexpr int BPW = 2 * KBLK / kWaves;       // blocks per wave
+    static constexpr int PART = KBLK * 1024;            // bytes of K (or of V^T)
+};
+
+// Per-lane source offsets of this wave's DMA blocks.  LDS byte 16 l of a
+// block receives lane l's 16 bytes, so each lane fetches the global chunk
+// that the swizzle puts there.
+template <int D>
+struct DmaPlan {
+    const char *base;            // K of head h, or V^T of head h
+    bool is_v;                   // wave-uniform
+    int off[Stage<D>::BPW];      // byte offset of the lane's chunk within a stage
+};
+
+template <int D>
+__device__ __forceinline__ void make_plan(DmaPlan<D> &pl, const uint16_t *Kp, const uint16_t *Vt,
+                                          const Layout &L, int h, int wave, int lane)
 {
-    constexpr int RCK = D / 8;                   // 16-byte chunks per K row
-    constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
-    constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
-    // Uniform bases of the stage in the permuted K and transposed V.
-    const char *kbase = (const char *)(Kp + ((long long)h * L.Npad + (long long)j * kTile + half * kStage) * D);
-    const char *vbase = (const char *)(Vt + ((long long)h * L.nT + j) * D * kTile + half * kStage);
+    constexpr int RCK = Stage<D>::RCK, KBLK = Stage<D>::KBLK, BPW = Stage<D>::BPW;
+    pl.is_v = wave * BPW >= KBLK;
+    pl.base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
+                      : (const char *)(Kp + (long long)h * L.Npad * D);
     const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
-        const int blk = wave * BPW + t;  // wave-uniform
-        const int kb = blk < KBLK ? blk : blk - KBLK;
+        const int blk = wave * BPW + t;
+        const int kb = pl.is_v ? blk - KBLK : blk;
         const int line = 4 * kb + line_in_blk;
         const int logical = phys ^ (line & 15);
-        const char *src;
-        if (blk < KBLK) {
+        if (!pl.is_v) {
             constexpr int RPL = 16 / RCK;
             const int row = RPL * line + logical / RCK, c = logical % RCK;
-            src = kbase + (row * D * 2 + 16 * c);
+            pl.off[t] = row * D * 2 + 16 * c;
         } else {
             const int dv = 2 * line + (logical >> 3), c = logical & 7;
-            src = vbase + (dv * kTile * 2 + 16 * c);
+            pl.off[t] = dv * kTile * 2 + 16 * c;
         }
-        __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (void __attribute__((address_space(3))) *)(stage + blk * 1024),
-                                         16, 0, 0);
     }
+}
+
+// Byte offset of stage (key tile j, half `half`) from the plan's base.
+template <int D>
+__device__ __forceinline__ long long stage_offset(const DmaPlan<D> &pl, int j, int half)
+{
+    return pl.is_v ? ((long long)j * D * kTile + half * kStage) * 2
+                   : ((long long)j * kTile + half * kStage) * D * 2;
+}
+
+// Issue this wave's DMA block t of a stage whose K goes to Kd and V^T to Vd.
+template <int D>
+__device__ __forceinline__ void issue_block(const DmaPlan<D> &pl, char *Kd, char *Vd, const char *src,
+                                            int wave, int t)
+{
+    const int blk = wave * Stage<D>::BPW + t;
+    lds_char *dst = pl.is_v ? (lds_char *)Vd + (blk - Stage<D>::KBLK) * 1024 : (lds_char *)Kd + blk * 1024;
+    __builtin_amdgcn_global_load_lds((const void *)(src + pl.off[t]), dst, 16, 0, 0);
 }
 
 // The per-wave state of one query block: 32 queries x D features.
@@ -152,54 +190,120 @@ struct RowState {
     float m, l;  // running max (log2 units) and partial row sum of this lane
 };
 
-// Attention of this wave's 32 queries to the kv real keys (1..64) of the
-// stage held in LDS at Ks (K) and Ks + K_BYTES (V^T).
-template <int D>
-__device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[D / 16], int kv,
-                                             float sl2, int prow, int l32, int hi, RowState<D> &st)
-{
-    constexpr int KS = D / 16, NB = D / 32, RCK = D / 8;
-    constexpr int K_BYTES = kStage * D * 2;
-    const char *Vs = Ks + K_BYTES;
-    const bool two = kv > 32;
+// Scores of this wave's 32 queries against the keys of one stage, S^T =
+// K Q^T as two 32-key halves (result register j of lane l: key
+// 16 (j / 8) + 8 (l / 32) + j % 8 of the half, query l % 32).
+struct Scores {
     f32x16 s0, s1;
+};
+// Probabilities in bf16, in the B-operand order of O^T += V^T P^T: 16-key
+// steps 0..3 of the stage.
+struct Probs {
+    bf16x8 p[4];
+};
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+// S = K Q^T for the kv real keys (1..64) of the stage whose K is at Ks; keys
+// past kv score -inf.  dma(t) issues this wave's DMA block t of a later
+// stage; the calls are spread over the products so the copies queue behind
+// matrix work instead of leaving in one burst.
+template <int D, typename Dma>
+__device__ __forceinline__ void qk_stage(Scores &S, const char *Ks, const bf16x8 (&qf)[D / 16],
+                                         const int (&kofs)[D / 16], int kv, int hi, Dma &&dma)
+{
+    constexpr int KS = D / 16;
+    constexpr int SUB1 = 64 * D;  // second 32-key half: 32 rows further on, same swizzle
+    constexpr int PER = KS / Stage<D>::BPW;
+    static_assert(PER * Stage<D>::BPW == KS, "DMA blocks must spread evenly over the k-steps");
+    const bool two = kv > 32;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
-        s0[jj] = 0.f;
-        s1[jj] = 0.f;
+        S.s0[jj] = 0.f;
+        S.s1[jj] = 0.f;
     }
+    // Operands are read one k-step ahead of the products that use them, so
+    // the LDS latency hides behind two matrix instructions.
     if (two) {
+        bf16x8 a0 = *(const bf16x8 *)(Ks + kofs[0]);
+        bf16x8 a1 = *(const bf16x8 *)(Ks + SUB1 + kofs[0]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a0 = *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi));
-            const bf16x8 a1 = *(const bf16x8 *)(Ks + lds_off<RCK>(32 + prow, 2 * ks + hi));
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+            bf16x8 n0, n1;
+            if (ks + 1 < KS) {
+                n0 = *(const bf16x8 *)(Ks + kofs[ks + 1]);
+                n1 = *(const bf16x8 *)(Ks + SUB1 + kofs[ks + 1]);
+            }
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
+            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], S.s1, 0, 0, 0);
+            if (ks % PER == PER - 1)
+                dma(ks / PER);
+            if (ks + 1 < KS) {
+                a0 = n0;
+                a1 = n1;
+            }
+        }
+        // Keep that order: reads of step ks + 1, then the products of ks.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
         }
     } else {
+        bf16x8 a0 = *(const bf16x8 *)(Ks + kofs[0]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi)), qf[ks], s0, 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 n0;
+            if (ks + 1 < KS)
+                n0 = *(const bf16x8 *)(Ks + kofs[ks + 1]);
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
+            if (ks % PER == PER - 1)
+                dma(ks / PER);
+            if (ks + 1 < KS)
+                a0 = n0;
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        }
     }
     if (kv < kStage) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
             const int key = 16 * (jj >> 3) + 8 * hi + (jj & 7);
             if (key >= kv)
-                s0[jj] = -INFINITY;
+                S.s0[jj] = -INFINITY;
             if (32 + key >= kv)
-                s1[jj] = -INFINITY;
+                S.s1[jj] = -INFINITY;
         }
     }
-    float mx = s0[0];
+}
+
+// Online softmax step: scores -> bf16 probabilities, running max and row sum
+// updated, accumulator rescaled when the max moves.  dma(t) as in qk_stage,
+// spread over the exponentials.
+template <int D, typename Dma>
+__device__ __forceinline__ void softmax_stage(Probs &P, const Scores &S, int kv, float sl2,
+                                              RowState<D> &st, Dma &&dma)
+{
+    constexpr int NB = D / 32;
+    constexpr int BPW = Stage<D>::BPW;
+    static_assert(BPW <= 4, "one DMA block per 16-key step at most");
+    const bool two = kv > 32;
+    float mx = S.s0[0];
 #pragma unroll
     for (int jj = 1; jj < 16; ++jj)
-        mx = fmaxf(mx, s0[jj]);
+        mx = fmaxf(mx, S.s0[jj]);
     if (two) {
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj)
-            mx = fmaxf(mx, s1[jj]);
+            mx = fmaxf(mx, S.s1[jj]);
     }
     // Running max in log2 units, moved lazily: only when some row's new
     // maximum exceeds it by more than kLazy, so the rescale of the
@@ -218,54 +322,99 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
             for (int jj = 0; jj < 16; ++jj)
                 st.acc[nb][jj] *= alpha;
     }
-    bf16x8 p0a, p0b, p1a, p1b;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        p0a[jj] = (__bf16)exp2_fast(fmaf(s0[jj], sl2, -st.m));
-        p0b[jj] = (__bf16)exp2_fast(fmaf(s0[jj + 8], sl2, -st.m));
-    }
-    st.l = row_sum_bf16(p0a, row_sum_bf16(p0b, st.l));
-    if (two) {
+    for (int q = 0; q < 4; ++q) {
+        if (q < 2 || two) {
+            const f32x16 &src = q < 2 ? S.s0 : S.s1;
+            const int o = (q & 1) * 8;
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            p1a[jj] = (__bf16)exp2_fast(fmaf(s1[jj], sl2, -st.m));
-            p1b[jj] = (__bf16)exp2_fast(fmaf(s1[jj + 8], sl2, -st.m));
+            for (int jj = 0; jj < 8; ++jj)
+                P.p[q][jj] = (__bf16)exp2_fast(fmaf(src[o + jj], sl2, -st.m));
+            st.l = row_sum_bf16(P.p[q], st.l);
         }
-        st.l = row_sum_bf16(p1a, row_sum_bf16(p1b, st.l));
-    }
-    // O^T += V^T P^T: A operand = V^T rows 32 nb + l32, keys in 16-key steps.
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 0 + hi)), p0a, st.acc[nb], 0, 0, 0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 2 + hi)), p0b, st.acc[nb], 0, 0, 0);
-    if (two) {
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 4 + hi)), p1a, st.acc[nb], 0, 0, 0);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 6 + hi)), p1b, st.acc[nb], 0, 0, 0);
+        if (q < BPW)
+            dma(q);
     }
 }
 
-// Wait for this wave's outstanding vector-memory operations (the stage DMA),
-// leaving LDS and scalar counters alone.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// O^T += V^T P^T over the stage whose V^T is at Vs (kv real keys).
+template <int D>
+__device__ __forceinline__ void pv_stage(const char *Vs, const int (&vofs)[4], const Probs &P, int kv,
+                                         RowState<D> &st)
+{
+    constexpr int NB = D / 32;
+    const int steps = kv > 32 ? 4 : 2;
+    // A operand = V^T rows 32 nb + l32, keys in 16-key steps (rows 32 apart
+    // are 16 swizzle lines apart: same pattern, 4 KB on).  The operands of
+    // a key step are read while the products of the previous one run.
+    bf16x8 va[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        va[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs[0]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q < steps) {
+            bf16x8 vn[NB];
+            if (q + 1 < steps) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    vn[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs[q + 1]);
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[nb], P.p[q], st.acc[nb], 0, 0, 0);
+            if (q + 1 < steps) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    va[nb] = vn[nb];
+            }
+        }
+    }
+    if (steps == 4) {
+        // Keep that order: reads of step q + 1, then the products of q.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q + 1 < 4)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NB, 0);
+        }
+    }
+}
+
+// s_waitcnt on this wave's vector-memory counter only (gfx9 encoding: vmcnt
+// in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier that waits for this wave's LDS operations but leaves its
+// DMA copies in flight (__syncthreads would drain those as well).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(Layout L, AttnParams P)
+__global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnParams P)
 {
     constexpr int KS = D / 16;
     constexpr int NB = D / 32;
-    constexpr int STAGE_BYTES = 2 * kStage * D * 2;
-    __shared__ __attribute__((aligned(1024))) char buf0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char buf1[STAGE_BYTES];
+    constexpr int BPW = Stage<D>::BPW;
+    constexpr int SB = Stage<D>::PART;
+    // The ring: stage slot k holds K in Kk and V^T in Vk.
+    __shared__ __attribute__((aligned(1024))) char K0[SB];
+    __shared__ __attribute__((aligned(1024))) char K1[SB];
+    __shared__ __attribute__((aligned(1024))) char K2[SB];
+    __shared__ __attribute__((aligned(1024))) char K3[SB];
+    __shared__ __attribute__((aligned(1024))) char V0[SB];
+    __shared__ __attribute__((aligned(1024))) char V1[SB];
+    __shared__ __attribute__((aligned(1024))) char V2[SB];
+    __shared__ __attribute__((aligned(1024))) char V3[SB];
     __shared__ int clist[kList];
 
     const uint16_t *__restrict__ Qp = (const uint16_t *)P.q;
@@ -274,8 +423,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(Layout L, AttnPa
     uint16_t *__restrict__ Op = (uint16_t *)P.o;
     const int *__restrict__ cols = P.cols;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
     const int l32 = lane & 31, hi = lane >> 5;
+    const int side = wave >> 2;  // query tile of the pair this wave serves
+    const int sub = wave & 3;    // its 32-query block within that tile
 
     // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD
     // contiguous chunks of the work order.
@@ -290,19 +442,28 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(Layout L, AttnPa
         }
     }
     const int r = P.order[w];
-    const int h = r / L.nT, i = r - h * L.nT;
-    const int ci = tile_tokens(L, P, i);
-    const bool wave_active = wave * 32 < ci;
+    const int h = r / L.nP;
+    const TilePair tp = pair_tiles(L, r - h * L.nP);
+    const int i = side ? tp.t2 : tp.t1;
+    const int ci = i >= 0 ? tile_tokens(L, P, i) : 0;
+    const bool wave_active = sub * 32 < ci;
+    const int my_bit = 1 << side;
 
     // Q operand (B of S^T = K Q^T): lane holds query l32, features
     // 16 ks + 8 hi .. +7 for every k-step.
-    const long long qrow = (long long)h * L.Npad + (long long)i * kTile + wave * 32 + l32;
+    const long long qrow = (long long)h * L.Npad + (long long)max(i, 0) * kTile + sub * 32 + l32;
     bf16x8 qf[KS];
-    {
+    if (wave_active) {
         const bf16x8 *qp = (const bf16x8 *)(Qp + qrow * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = qp[2 * ks + hi];
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                qf[ks][u] = (__bf16)0.0f;
     }
     RowState<D> st;
 #pragma unroll
@@ -317,71 +478,178 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(Layout L, AttnPa
     const int beg = P.row_ptr[r];
     const int end = (int)min((long long)P.row_ptr[r + 1], P.cap);
 
-    // The row's key-tile ids, staged in LDS (kList at a time; longer rows
-    // refill the list when the cursor reaches its end).
-    int list_base = beg, list_end = beg;
-    auto fill_list = [&](int from) {
-        list_base = from;
-        list_end = min(end, from + kList);
-        for (int u = tid; u < list_end - list_base; u += kThreads)
-            clist[u] = cols[list_base + u];
+    // The pair's list entries, staged in LDS as a ring of two halves: entry
+    // idx lives at clist[(idx - beg) % kList].  The first kList entries are
+    // loaded up front.  When a wave's cursor reaches the middle of the k-th
+    // kHalf entries (k >= 1), that wave loads its share of the next kHalf
+    // entries into the other half, which every cursor has left by then
+    // (cursors differ by at most one entry); hundreds of barriers pass
+    // before any cursor gets there, so no barrier of its own is needed.
+    constexpr int kHalf = kList / 2;
+    {
+        const int n = min(end - beg, kList);
+        for (int u = tid; u < n; u += kThreads)
+            clist[u] = cols[beg + u];
         __syncthreads();
-    };
-
-    // Stage cursor: key tile idx (id j, c real tokens) and which half of it.
-    int idx = beg, half = 0, j = 0, c = 0;
-    if (idx < end) {
-        fill_list(beg);
-        j = clist[0];
-        c = tile_tokens(L, P, j);
-        issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, 0, wave, lane);
     }
-    const int prow = key_of_mfma_row(l32);
+    auto refill = [&](int first) {  // entries [first, first + kHalf) of the list
+        for (int u = wave * 64 + lane; u < kHalf; u += kThreads) {
+            const int e = first + u;
+            if (e < end)
+                clist[(e - beg) & (kList - 1)] = cols[e];
+        }
+    };
+    static_assert((kList & (kList - 1)) == 0, "ring index by mask");
 
-    // Advance the cursor by one stage (all waves together, after a barrier).
-    auto advance = [&]() {
+    DmaPlan<D> plan;
+    make_plan<D>(plan, Kp, Vt, L, h, wave, lane);
+
+    // Stage cursor (per wave; every wave takes the same stages in the same
+    // order): entry idx = key tile j with c real keys and keep bits `bits`,
+    // and which 64-key half of it.
+    int idx = beg, half = 0, j = 0, c = 0, bits = 0;
+    auto load_entry = [&]() {
+        const int rel = idx - beg;
+        if (rel >= kList - kHalf / 2 && (rel & (kHalf - 1)) == kHalf / 2)
+            refill(idx + kHalf / 2);
+        const int e = clist[rel & (kList - 1)];
+        j = e & kPairTileMask;
+        bits = (int)((unsigned)e >> kPairShift);
+        c = tile_tokens(L, P, j);
+    };
+    if (idx < end)
+        load_entry();
+    // Takes the next stage: returns its descriptor (kv | bits << 8 | 1 << 10;
+    // 0 past the end) and the source of this wave's part of it.  Past the end
+    // the source is the head's first stage, always in bounds; that copy lands
+    // in a slot nobody reads again.
+    auto take = [&](const char *&src) -> int {
+        if (idx >= end) {
+            src = plan.base;
+            return 0;
+        }
+        const int kv = min(kStage, c - half * kStage);
+        src = plan.base + stage_offset<D>(plan, j, half);
+        const int desc = kv | (bits << 8) | (1 << 10);
         if (half == 0 && c > kStage) {
             half = 1;
         } else {
             ++idx;
             half = 0;
-            if (idx < end) {
-                if (idx == list_end) {
-                    __syncthreads();  // every wave is done reading the list
-                    fill_list(idx);
-                }
-                j = clist[idx - list_base];
-                c = tile_tokens(L, P, j);
-            }
+            if (idx < end)
+                load_entry();
         }
+        return desc;
     };
-
-    while (idx < end) {
-        // ---- stage in buf0
-        {
-            const int kv = min(kStage, c - half * kStage);
-            wait_vmem();
-            __syncthreads();  // buf0 complete; buf1 free
-            advance();
-            if (idx < end)
-                issue_stage<D>((lds_char *)buf1, Kp, Vt, L, h, j, half, wave, lane);
-            if (wave_active)
-                attend_stage<D>(buf0, qf, kv, sl2, prow, l32, hi, st);
-        }
-        if (idx >= end)
-            break;
-        // ---- stage in buf1
-        {
-            const int kv = min(kStage, c - half * kStage);
-            wait_vmem();
-            __syncthreads();  // buf1 complete; buf0 free
-            advance();
-            if (idx < end)
-                issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, half, wave, lane);
-            if (wave_active)
-                attend_stage<D>(buf1, qf, kv, sl2, prow, l32, hi, st);
-        }
+    // Per-lane LDS offsets of the MFMA operands within a stage: K chunk
+    // 2 ks + hi of row key_of_mfma_row(l32), and V^T chunk 2 q + hi of row l32.
+    int kofs[KS], vofs[4];
+    {
+        const int prow = key_of_mfma_row(l32);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kofs[ks] = lds_off<D / 8>(prow, 2 * ks + hi);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            vofs[q] = lds_off<8>(l32, 2 * q + hi);
     }
+
+    // Ping-pong schedule.  Group A (waves 0-3, first query tile) and group B
+    // (waves 4-7, second tile) share the stages; each SIMD hosts one wave of
+    // each.  Every wave runs the same steps, one per stage s:
+    //
+    //   [barrier] O += P V (s-1), S = K Q^T (s)   [barrier] softmax (s)
+    //
+    // but B passes one extra barrier first, so it runs half a step behind A:
+    // while one wave of a SIMD issues matrix products the other runs its
+    // exponentials.  Stage t lives in ring slot t % 4; its K is read in A's
+    // and then B's step t, its V^T in their steps t + 1.  Each wave copies
+    // its share of stage s + 2 (K by group A, V^T by group B, BPW blocks per
+    // wave) in step s, into the slot of stage s - 2, which B finished with
+    // in its step s - 1, before A's step s began.  At the top of step s a
+    // wave waits for its copies of stage s (those of s + 1 may still fly):
+    // for A that is K(s), needed now; for B, V^T(s), first needed in A's
+    // step s + 1, which starts after B's step s began.
+    // Descriptors: kv | bits << 8 | 1 << 10 (0: no such stage).
+    // The cursor runs one stage ahead of the copies: the stage copied in
+    // step s is taken in step s - 1, after the softmax barrier, so its
+    // scalar work and list read sit in the exponential phase and not in
+    // front of the matrix products.
+    int d0, d1, d2;
+    const char *src2;
+    {
+        const char *src;
+        d0 = take(src);
+#pragma unroll
+        for (int t = 0; t < BPW; ++t)
+            issue_block<D>(plan, K0, V0, src, wave, t);
+        d1 = take(src);
+#pragma unroll
+        for (int t = 0; t < BPW; ++t)
+            issue_block<D>(plan, K1, V1, src, wave, t);
+        d2 = take(src2);
+    }
+    auto attends = [&](int d) { return wave_active && ((d >> 8) & my_bit); };
+    Scores S;
+    Probs Pr;
+    // Step s: K(s) in Kc, V^T(s-1) in Vp; stage s+2 (source src) goes to Kn,
+    // Vn; stage s+3 is taken into dnext, src.  Returns whether stage s
+    // existed (otherwise the step only finished s-1).  The slots are
+    // distinct arrays addressed statically, so the compiler can tell the
+    // reads of one slot from the copies in flight to the others.
+    auto step = [&](const char *Kc, const char *Vp, char *Kn, char *Vn, int dprev, int dcur,
+                    const char *&src, int &dnext) {
+        // Hide the operand offsets from loop-invariant hoisting: otherwise
+        // the compiler keeps a full set of addresses per slot live across
+        // the loop and runs out of registers.  Recomputing them costs one
+        // add per offset per step.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            asm volatile("" : "+v"(kofs[ks]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            asm volatile("" : "+v"(vofs[q]));
+        wait_vmcnt<BPW>();
+        lds_barrier();
+        const char *const from = src;
+        auto dma = [&](int t) { issue_block<D>(plan, Kn, Vn, from, wave, t); };
+        if (attends(dprev))
+            pv_stage<D>(Vp, vofs, Pr, dprev & 255, st);
+        if (attends(dcur)) {
+            qk_stage<D>(S, Kc, qf, kofs, dcur & 255, hi, dma);
+        } else {
+#pragma unroll
+            for (int t = 0; t < BPW; ++t)
+                dma(t);
+        }
+        lds_barrier();
+        dnext = take(src);
+        if (attends(dcur))
+            softmax_stage<D>(Pr, S, dcur & 255, sl2, st, [](int) {});
+        return dcur != 0;
+    };
+    if (side == 1)
+        lds_barrier();
+    int dm1 = 0;
+    const char *src = src2;
+    for (;;) {
+        int d3;
+        if (!step(K0, V3, K2, V2, dm1, d0, src, d3))
+            break;
+        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
+        if (!step(K1, V0, K3, V3, dm1, d0, src, d3))
+            break;
+        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
+        if (!step(K2, V1, K0, V0, dm1, d0, src, d3))
+            break;
+        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
+        if (!step(K3, V2, K1, V1, dm1, d0, src, d3))
+            break;
+        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
+    }
+    if (side == 0)
+        lds_barrier();  // pairs with B's extra barrier: both groups pass the same count
+    wait_vmcnt<0>();  // no copy may land after the workgroup ends
 
     if (wave_active) {
         const float lt = half_sum(st.l);
@@ -410,7 +678,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_mfma_kernel(Layout L, AttnPa
 
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s)
 {
-    const dim3 grid(L.heads * L.nT);
+    const dim3 grid(L.heads * L.nP);
     if (L.D == 128)
         hipLaunchKernelGGL(attn_mfma_kernel<128>, grid, dim3(kThreads), 0, s, L, p);
     else

@@ -26,6 +26,13 @@ struct Layout {
     int D;            // head dim
     long long N;      // tokens
     long long Npad;   // slots = nT * B
+    // Query-tile pairs.  The matrix-core kernel runs two query tiles of one
+    // head per workgroup, over the union of their key lists.  Tiles pair up
+    // along axis pax (0 = t, 1 = y, 2 = x) as coordinates (2c, 2c + 1); a
+    // last tile on an odd axis is alone.  pax = -1: no pairing.
+    int pax;
+    int pn[3];        // pair grid (tile grid with the paired axis halved)
+    int nP;           // pairs per head
 };
 
 // Clipped extents of tile tau along t, y, x.
@@ -51,6 +58,43 @@ __host__ __device__ inline int tile_real_count(const Layout &L, int tau)
     TileBox r = tile_box(L, tau);
     return r.et * r.ey * r.ex;
 }
+
+// The query tiles of pair pr (raster over the pair grid); t2 = -1 when the
+// first tile is alone.
+struct TilePair {
+    int t1, t2;
+};
+
+__host__ __device__ inline TilePair pair_tiles(const Layout &L, int pr)
+{
+    int a = pr / (L.pn[1] * L.pn[2]);
+    int b = (pr / L.pn[2]) % L.pn[1];
+    int e = pr % L.pn[2];
+    int a2 = a, b2 = b, e2 = e;
+    bool two = false;
+    if (L.pax == 0) {
+        a *= 2;
+        a2 = a + 1;
+        two = a2 < L.nt;
+    } else if (L.pax == 1) {
+        b *= 2;
+        b2 = b + 1;
+        two = b2 < L.ny;
+    } else if (L.pax == 2) {
+        e *= 2;
+        e2 = e + 1;
+        two = e2 < L.nx;
+    }
+    TilePair r;
+    r.t1 = (a * L.ny + b) * L.nx + e;
+    r.t2 = two ? (a2 * L.ny + b2) * L.nx + e2 : -1;
+    return r;
+}
+
+// Pair-list entries hold the key tile in the low 30 bits and, in bits 30 and
+// 31, whether the first and the second query tile of the pair keep it.
+constexpr int kPairShift = 30;
+constexpr int kPairTileMask = (1 << kPairShift) - 1;
 
 // Division of 0 <= n < 2^31 by a fixed divisor 1 <= d < 2^31 with one
 // multiply-high, add and shift: the round-up method of Granlund and
@@ -103,19 +147,22 @@ struct MaskBuffers {
     long long cap;
     int R;
     int nchunks;
+    int pair;       // 0: rows r = h nT + i; 1: pairs r = h nP + pr (entries carry keep bits)
 };
 
 constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
 
+// Compiles the mask into mb; then, when pb.R > 0, into the pair lists pb
+// (which share mb's groups).
 hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
-                               const MaskBuffers &mb, hipStream_t s);
+                               const MaskBuffers &mb, const MaskBuffers &pb, hipStream_t s);
 
 struct AttnParams {
     const void *q;      // tile-major rows
     const void *k;      // tile-major rows
     const void *v;      // tile-major rows (generic) or tile columns (MFMA)
     void *o;            // tile-major rows
-    const int *row_ptr;
+    const int *row_ptr; // generic kernel: rows; matrix-core kernel: pairs
     const int *cols;
     const int *order;
     long long cap;      // valid entries of cols
@@ -125,7 +172,7 @@ struct AttnParams {
     FastDiv div_row;    // nx: tiles per tile-grid row
 };
 
-// bf16 matrix-core kernel: B == 128, D in {64, 128}.
+// bf16 matrix-core kernel over query-tile pairs: B == 128, D in {64, 128}.
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
 // fp32 vector-ALU kernel for any supported shape; elem_bytes 4 (fp32) or 2 (bf16).
 hipError_t launch_attention_generic(const Layout &L, int elem_bytes, const AttnParams &p,

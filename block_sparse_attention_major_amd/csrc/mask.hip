@@ -20,6 +20,12 @@
 //            bucket starts of each length in decreasing order; per-chunk bases
 //   fill   : one wave per row -> ascending key-tile ids
 //   order  : one workgroup per chunk -> order[base + rank among equal lengths]
+//
+// The matrix-core attention kernel reads pair lists instead: the same stages
+// run over query-tile pairs r = h nP + pr (pair_tiles), keeping key tile j
+// when either tile of the pair keeps it, and each entry carries which of the
+// two does (j | bits << kPairShift).  The row lists stay the mask's
+// definitive form (they are what the index-list hook returns).
 #include "common.h"
 
 namespace sa {
@@ -29,20 +35,18 @@ namespace {
 constexpr int kWave = 64;
 
 struct RowCtx {
-    int h, ai, bi, ei;
-    int g0, g1;  // group range of head h
+    int ai, bi, ei;  // query tile coordinates
+    int g0, g1;      // group range of the head
 };
 
-__device__ __forceinline__ RowCtx row_ctx(const Layout &L, const MaskBuffers &mb, int r)
+__device__ __forceinline__ RowCtx tile_ctx(const Layout &L, const MaskBuffers &mb, int h, int i)
 {
     RowCtx c;
-    c.h = r / L.nT;
-    const int i = r - c.h * L.nT;
     c.ai = i / (L.ny * L.nx);
     c.bi = (i / L.nx) % L.ny;
     c.ei = i % L.nx;
-    c.g0 = mb.group_off[c.h];
-    c.g1 = mb.group_off[c.h + 1];
+    c.g0 = mb.group_off[h];
+    c.g1 = mb.group_off[h + 1];
     return c;
 }
 
@@ -65,12 +69,49 @@ __device__ __forceinline__ bool window_keeps(const Layout &L, const MaskBuffers 
 
 template <int KIND>
 __device__ __forceinline__ bool keeps(const Layout &L, const MaskBuffers &mb,
-                                      const uint8_t *__restrict__ bitmap, const RowCtx &c, int r,
-                                      int j)
+                                      const uint8_t *__restrict__ bitmap, const RowCtx &c, int h,
+                                      int i, int j)
 {
     if (KIND == 0)
-        return bitmap[(long long)r * L.nT + j] != 0;
+        return bitmap[((long long)h * L.nT + i) * L.nT + j] != 0;
     return window_keeps(L, mb, c, j);
+}
+
+// The query tiles behind list r: one tile for a row list, two (t2 = -1: one)
+// for a pair list.
+struct ListRow {
+    int h, t1, t2;
+    RowCtx c1, c2;
+};
+
+__device__ __forceinline__ ListRow list_row(const Layout &L, const MaskBuffers &mb, int r)
+{
+    ListRow q;
+    if (mb.pair) {
+        q.h = r / L.nP;
+        const TilePair tp = pair_tiles(L, r - q.h * L.nP);
+        q.t1 = tp.t1;
+        q.t2 = tp.t2;
+    } else {
+        q.h = r / L.nT;
+        q.t1 = r - q.h * L.nT;
+        q.t2 = -1;
+    }
+    q.c1 = tile_ctx(L, mb, q.h, q.t1);
+    q.c2 = tile_ctx(L, mb, q.h, q.t2 >= 0 ? q.t2 : q.t1);
+    return q;
+}
+
+// Keep bits of key tile j for list r: bit 0 = first query tile, bit 1 =
+// second.  A row list only has bit 0.
+template <int KIND>
+__device__ __forceinline__ int keep_bits(const Layout &L, const MaskBuffers &mb,
+                                         const uint8_t *__restrict__ bitmap, const ListRow &q, int j)
+{
+    int bits = keeps<KIND>(L, mb, bitmap, q.c1, q.h, q.t1, j) ? 1 : 0;
+    if (q.t2 >= 0 && keeps<KIND>(L, mb, bitmap, q.c2, q.h, q.t2, j))
+        bits |= 2;
+    return bits;
 }
 
 __global__ void zero_kernel(int *__restrict__ p, long long n)
@@ -88,10 +129,10 @@ __global__ __launch_bounds__(256) void count_kernel(Layout L, MaskBuffers mb,
     if (r >= mb.R)
         return;
     const int lane = threadIdx.x & 63;
-    const RowCtx c = row_ctx(L, mb, r);
+    const ListRow q = list_row(L, mb, r);
     int n = 0;
     for (int j = lane; j < L.nT; j += kWave)
-        n += keeps<KIND>(L, mb, bitmap, c, r, j) ? 1 : 0;
+        n += keep_bits<KIND>(L, mb, bitmap, q, j) ? 1 : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1)
         n += __shfl_xor(n, off);
@@ -178,16 +219,16 @@ __global__ __launch_bounds__(256) void fill_kernel(Layout L, MaskBuffers mb,
     if (r >= mb.R)
         return;
     const int lane = threadIdx.x & 63;
-    const RowCtx c = row_ctx(L, mb, r);
+    const ListRow q = list_row(L, mb, r);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     long long base = mb.row_ptr[r];
     for (int j0 = 0; j0 < L.nT; j0 += kWave) {
         const int j = j0 + lane;
-        const bool keep = j < L.nT && keeps<KIND>(L, mb, bitmap, c, r, j);
-        const unsigned long long bits = __ballot(keep);
+        const int kb = j < L.nT ? keep_bits<KIND>(L, mb, bitmap, q, j) : 0;
+        const unsigned long long bits = __ballot(kb != 0);
         const long long pos = base + __popcll(bits & below);
-        if (keep && pos < mb.cap)
-            mb.cols[pos] = j;
+        if (kb && pos < mb.cap)
+            mb.cols[pos] = mb.pair ? (int)((unsigned)j | ((unsigned)kb << kPairShift)) : j;
         base += __popcll(bits);
     }
 }
@@ -211,12 +252,13 @@ __global__ __launch_bounds__(kMaskChunk) void order_kernel(Layout L, MaskBuffers
 
 }  // namespace
 
-hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
-                               const MaskBuffers &mb, hipStream_t s)
+namespace {
+
+hipError_t compile_lists(const Layout &L, int kind, const uint8_t *bitmap, const MaskBuffers &mb,
+                         hipStream_t s)
 {
     const long long nchunk_words = (long long)mb.nchunks * (L.nT + 1);
     hipLaunchKernelGGL(zero_kernel, dim3(256), dim3(256), 0, s, mb.chunk, nchunk_words);
-    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, mb.status, 16ll);
     const dim3 rows_grid((mb.R + 3) / 4);
     if (kind == 0)
         hipLaunchKernelGGL(count_kernel<0>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
@@ -229,6 +271,19 @@ hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
         hipLaunchKernelGGL(fill_kernel<1>, rows_grid, dim3(256), 0, s, L, mb, bitmap);
     hipLaunchKernelGGL(order_kernel, dim3(mb.nchunks), dim3(kMaskChunk), 0, s, L, mb);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
+                               const MaskBuffers &mb, const MaskBuffers &pb, hipStream_t s)
+{
+    // Status words of both list sets share one 16-word block.
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(64), 0, s, mb.status, 16ll);
+    hipError_t e = compile_lists(L, kind, bitmap, mb, s);
+    if (e == hipSuccess && pb.R > 0)
+        e = compile_lists(L, kind, bitmap, pb, s);
+    return e;
 }
 
 }  // namespace sa

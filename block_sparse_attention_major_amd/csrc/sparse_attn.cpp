@@ -21,7 +21,8 @@ struct sparse_attn_handle {
     float scale;
     // compiled mask
     bool has_mask = false;
-    sa::MaskBuffers mb{};
+    sa::MaskBuffers mb{};  // row lists
+    sa::MaskBuffers pb{};  // pair lists (matrix-core kernel only; R = 0 otherwise)
     // host copy of the last dual-window spec (source of the upload)
     std::vector<int32_t> spec;
     std::string err;
@@ -58,17 +59,24 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
-// Mask-buffer carving.
+// Mask-buffer carving: row-list arrays, then (matrix-core kernel) pair-list
+// arrays, then the row index list [cap] and (matrix-core kernel) the pair
+// index list [cap].  A pair list is never longer than the two row lists it
+// merges, so cap entries hold it whenever they hold the rows.
 struct MaskLayout {
-    size_t row_ptr, len, order, chunk, bucket, status, groups, group_off, cols;
-    int R, nchunks;
+    size_t row_ptr, len, order, chunk, bucket, status, groups, group_off;
+    size_t p_row_ptr, p_len, p_order, p_chunk, p_bucket;
+    size_t cols;  // start of the index lists
+    int R, nchunks, P, pnchunks;
 };
 
-MaskLayout mask_layout(const sa::Layout &L)
+MaskLayout mask_layout(const sa::Layout &L, bool pairs)
 {
     MaskLayout m{};
     m.R = L.heads * L.nT;
     m.nchunks = (m.R + sa::kMaskChunk - 1) / sa::kMaskChunk;
+    m.P = pairs ? L.heads * L.nP : 0;
+    m.pnchunks = (m.P + sa::kMaskChunk - 1) / sa::kMaskChunk;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -83,8 +91,22 @@ MaskLayout mask_layout(const sa::Layout &L)
     m.status = take(64);
     m.groups = take(4 * 6 * size_t(L.heads) * SPARSE_ATTN_MAX_GROUPS);
     m.group_off = take(4 * size_t(L.heads + 1));
+    if (pairs) {
+        m.p_row_ptr = take(4 * size_t(m.P + 1));
+        m.p_len = take(4 * size_t(m.P));
+        m.p_order = take(4 * size_t(m.P));
+        m.p_chunk = take(4 * size_t(m.pnchunks) * size_t(L.nT + 1));
+        m.p_bucket = take(4 * size_t(L.nT + 1));
+    }
     m.cols = off;
     return m;
+}
+
+// Bytes of a mask buffer whose index lists hold cap entries.
+size_t mask_buffer_bytes(const MaskLayout &m, long long cap)
+{
+    const size_t rows_end = m.cols + 4 * size_t(cap);
+    return m.P > 0 ? sa::align256(rows_end) + 4 * size_t(cap) : rows_end;
 }
 
 long long max_pairs(const sa::Layout &L) { return (long long)L.heads * L.nT * L.nT; }
@@ -137,10 +159,11 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     p.k = b + w.k;
     p.v = b + w.v;
     p.o = b + w.o;
-    p.row_ptr = h->mb.row_ptr;
-    p.cols = h->mb.cols;
-    p.order = h->mb.order;
-    p.cap = h->mb.cap;
+    const sa::MaskBuffers &lists = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? h->pb : h->mb;
+    p.row_ptr = lists.row_ptr;
+    p.cols = lists.cols;
+    p.order = lists.order;
+    p.cap = lists.cap;
     p.scale_log2 = h->scale * 1.4426950408889634f;
     // Consecutive work items of one XCD take 32 consecutive (longest-first)
     // rows, so query tiles that share key tiles share that XCD's L2.
@@ -218,6 +241,22 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     L.D = c.head_dim;
     L.N = N;
     L.Npad = nT * B;
+    // Pair query tiles along y, t or x: an axis of even extent first (no
+    // tile left alone), preferring y, then t, then x.
+    {
+        const int n[3] = {L.nt, L.ny, L.nx};
+        const int pref[3] = {1, 0, 2};
+        L.pax = -1;
+        for (int a : pref)
+            if (L.pax < 0 && n[a] >= 2 && n[a] % 2 == 0)
+                L.pax = a;
+        for (int a : pref)
+            if (L.pax < 0 && n[a] >= 2)
+                L.pax = a;
+        for (int a = 0; a < 3; ++a)
+            L.pn[a] = a == L.pax ? (n[a] + 1) / 2 : n[a];
+        L.nP = L.pn[0] * L.pn[1] * L.pn[2];
+    }
 
     auto *h = new sparse_attn_handle();
     h->cfg = c;
@@ -260,7 +299,7 @@ int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t 
     if (!h || !bytes)
         return SPARSE_ATTN_INVALID_ARG;
     const long long cap = (max_nnz <= 0 || max_nnz > max_pairs(h->L)) ? max_pairs(h->L) : max_nnz;
-    *bytes = mask_layout(h->L).cols + 4 * size_t(cap);
+    *bytes = mask_buffer_bytes(mask_layout(h->L, h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16), cap);
     return SPARSE_ATTN_OK;
 }
 
@@ -282,9 +321,10 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
     if (!aligned16(mask_buf))
         return fail(h, SPARSE_ATTN_INVALID_ARG, "mask_buf is not 16-byte aligned");
     const sa::Layout &L = h->L;
-    const MaskLayout ml = mask_layout(L);
+    const bool pairs = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16;
+    const MaskLayout ml = mask_layout(L, pairs);
     const long long want = (m->max_nnz <= 0 || m->max_nnz > max_pairs(L)) ? max_pairs(L) : m->max_nnz;
-    const size_t need = ml.cols + 4 * size_t(want);
+    const size_t need = mask_buffer_bytes(ml, want);
     if (bytes < need)
         return fail(h, SPARSE_ATTN_WORKSPACE_TOO_SMALL, "mask_buf holds %zu bytes, %zu needed", bytes,
                     need);
@@ -345,9 +385,24 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
     mb.groups = reinterpret_cast<int *>(base + ml.groups);
     mb.group_off = reinterpret_cast<int *>(base + ml.group_off);
     mb.cols = reinterpret_cast<int *>(base + ml.cols);
-    mb.cap = std::min<long long>((bytes - ml.cols) / 4, max_pairs(L));
+    mb.cap = want;
     mb.R = ml.R;
     mb.nchunks = ml.nchunks;
+    mb.pair = 0;
+    sa::MaskBuffers pb{};
+    if (pairs) {
+        pb = mb;
+        pb.row_ptr = reinterpret_cast<int *>(base + ml.p_row_ptr);
+        pb.len = reinterpret_cast<int *>(base + ml.p_len);
+        pb.order = reinterpret_cast<int *>(base + ml.p_order);
+        pb.chunk = reinterpret_cast<int *>(base + ml.p_chunk);
+        pb.bucket = reinterpret_cast<int *>(base + ml.p_bucket);
+        pb.status = mb.status + 4;
+        pb.cols = reinterpret_cast<int *>(base + sa::align256(ml.cols + 4 * size_t(want)));
+        pb.R = ml.P;
+        pb.nchunks = ml.pnchunks;
+        pb.pair = 1;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     h->has_mask = false;
@@ -363,10 +418,11 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
             return hip_fail(h, e, "uploading the window spec");
     }
     const hipError_t e = sa::launch_compile_mask(
-        L, m->kind == SPARSE_ATTN_MASK_BITMAP ? 0 : 1, m->bitmap, mb, s);
+        L, m->kind == SPARSE_ATTN_MASK_BITMAP ? 0 : 1, m->bitmap, mb, pb, s);
     if (e != hipSuccess)
         return hip_fail(h, e, "mask compile launch");
     h->mb = mb;
+    h->pb = pb;
     h->has_mask = true;
     return SPARSE_ATTN_OK;
 }

@@ -159,7 +159,9 @@ void sparse_attn_destroy(sparse_attn_handle *h);
 int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *info);
 
 /* Device bytes the compiled-mask buffer needs for at most max_nnz kept tile
- * pairs (<= 0: heads * nT * nT).  Errors: INVALID_ARG. */
+ * pairs (<= 0: heads * nT * nT).  With the matrix-core kernel the buffer
+ * holds two index lists of max_nnz entries (rows and query-tile pairs, see
+ * sparse_attn_set_mask), otherwise one.  Errors: INVALID_ARG. */
 int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t *bytes);
 
 /* Device bytes of the forward workspace (permuted Q, K, V and O).
@@ -170,6 +172,9 @@ int sparse_attn_workspace_bytes(const sparse_attn_handle *h, size_t *bytes);
  * Compile a mask on the GPU into mask_buf: per query-tile row r = h nT + i
  * the kept key tiles in ascending order (row offsets by exclusive sum of row
  * lengths), and a work order of rows by decreasing length, ties by row id.
+ * With the matrix-core kernel it also compiles the same lists for pairs of
+ * neighbouring query tiles (union of the two rows, each entry marked with
+ * the tiles that keep it), which is what that kernel walks.
  * mask_buf (device, caller-owned, at least sparse_attn_mask_bytes(max_nnz)
  * bytes) must stay alive and unmodified while forwards use the mask; calling
  * again replaces the mask.  If the mask keeps more pairs than max_nnz, the

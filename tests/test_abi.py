@@ -56,12 +56,17 @@ def test_create_and_layout(sa):
     per = 40 * 80640 * 128 * 2
     assert L["ws_bytes"] == sa.sparse_attn_workspace_bytes(h) == 4 * per
     assert L["ws_offset_k"] == per and L["ws_offset_o"] == 3 * per
+    # The matrix-core kernel keeps two index lists (query-tile rows and
+    # query-tile pairs) of max_nnz entries each.
     full = sa.sparse_attn_mask_bytes(h)
-    assert full >= 40 * 630 * 630 * 4
-    assert sa.sparse_attn_mask_bytes(h, 1000) == full - 4 * (40 * 630 * 630 - 1000)
+    assert full >= 2 * 40 * 630 * 630 * 4
+    shrink = full - sa.sparse_attn_mask_bytes(h, 1000)
+    assert abs(shrink - 8 * (40 * 630 * 630 - 1000)) < 256
     sa.sparse_attn_destroy(h)
     tiny = sa.sparse_attn_create(2, 64, (4, 8, 8), (1, 4, 4), "f32")
     assert sa.sparse_attn_layout(tiny)["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    full = sa.sparse_attn_mask_bytes(tiny)
+    assert sa.sparse_attn_mask_bytes(tiny, 100) == full - 4 * (2 * 16 * 16 - 100)
 
 
 @pytest.mark.parametrize("kw,code", [
