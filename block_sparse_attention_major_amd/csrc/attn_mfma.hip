@@ -505,20 +505,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     make_plan<D>(plan, Kp, Vt, L, h, wave, lane);
 
     // Stage cursor (per wave; every wave takes the same stages in the same
-    // order): entry idx = key tile j with c real keys and keep bits `bits`,
-    // and which 64-key half of it.
-    int idx = beg, half = 0, j = 0, c = 0, bits = 0;
-    auto load_entry = [&]() {
-        const int rel = idx - beg;
+    // order): entry idx (packed, see pair_entry) and which 64-key half of
+    // its key tile.  The entry after it is read one take ahead, so the LDS
+    // latency of the list read hides behind a phase of other work.
+    int idx = beg, half = 0, e_cur = 0;
+    int e_next = 0;  // raw LDS read of entry idx + 1 (lanes agree)
+    auto read_entry = [&](int at) {
+        const int rel = at - beg;
         if (rel >= kList - kHalf / 2 && (rel & (kHalf - 1)) == kHalf / 2)
-            refill(idx + kHalf / 2);
-        const int e = clist[rel & (kList - 1)];
-        j = e & kPairTileMask;
-        bits = (int)((unsigned)e >> kPairShift);
-        c = tile_tokens(L, P, j);
+            refill(at + kHalf / 2);
+        return clist[rel & (kList - 1)];
     };
-    if (idx < end)
-        load_entry();
+    if (beg < end)
+        e_cur = __builtin_amdgcn_readfirstlane(read_entry(beg));
+    if (beg + 1 < end)
+        e_next = read_entry(beg + 1);
     // Takes the next stage: returns its descriptor (kv | bits << 8 | 1 << 10;
     // 0 past the end) and the source of this wave's part of it.  Past the end
     // the source is the head's first stage, always in bounds; that copy lands
@@ -528,6 +529,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
             src = plan.base;
             return 0;
         }
+        const int j = e_cur & 0xffff;
+        const int c = (e_cur >> kPairCountShift) & 255;
+        const int bits = (e_cur >> kPairBitsShift) & 3;
         const int kv = min(kStage, c - half * kStage);
         src = plan.base + stage_offset<D>(plan, j, half);
         const int desc = kv | (bits << 8) | (1 << 10);
@@ -536,8 +540,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         } else {
             ++idx;
             half = 0;
-            if (idx < end)
-                load_entry();
+            e_cur = __builtin_amdgcn_readfirstlane(e_next);
+            if (idx + 1 < end)
+                e_next = read_entry(idx + 1);
         }
         return desc;
     };
@@ -565,18 +570,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     // exponentials.  Stage t lives in ring slot t % 4; its K is read in A's
     // and then B's step t, its V^T in their steps t + 1.  Each wave copies
     // its share of stage s + 2 (K by group A, V^T by group B, BPW blocks per
-    // wave) in step s, into the slot of stage s - 2, which B finished with
-    // in its step s - 1, before A's step s began.  At the top of step s a
+    // wave) in the softmax half of its step s, into the slot of stage s - 2,
+    // which B finished with in its step s - 1.  At the top of step s a
     // wave waits for its copies of stage s (those of s + 1 may still fly):
     // for A that is K(s), needed now; for B, V^T(s), first needed in A's
     // step s + 1, which starts after B's step s began.
     // Descriptors: kv | bits << 8 | 1 << 10 (0: no such stage).
-    // The cursor runs one stage ahead of the copies: the stage copied in
-    // step s is taken in step s - 1, after the softmax barrier, so its
-    // scalar work and list read sit in the exponential phase and not in
-    // front of the matrix products.
-    int d0, d1, d2;
-    const char *src2;
+    int d0, d1;
     {
         const char *src;
         d0 = take(src);
@@ -587,18 +587,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
 #pragma unroll
         for (int t = 0; t < BPW; ++t)
             issue_block<D>(plan, K1, V1, src, wave, t);
-        d2 = take(src2);
     }
     auto attends = [&](int d) { return wave_active && ((d >> 8) & my_bit); };
     Scores S;
     Probs Pr;
-    // Step s: K(s) in Kc, V^T(s-1) in Vp; stage s+2 (source src) goes to Kn,
-    // Vn; stage s+3 is taken into dnext, src.  Returns whether stage s
-    // existed (otherwise the step only finished s-1).  The slots are
-    // distinct arrays addressed statically, so the compiler can tell the
-    // reads of one slot from the copies in flight to the others.
+    // Step s: K(s) in Kc, V^T(s-1) in Vp; stage s+2 is taken and copied to
+    // Kn, Vn at the start of the softmax phase, which has room for the
+    // scalar work and the copy issue while the other group's wave keeps the
+    // matrix core busy.  Returns whether stage s existed (otherwise the step
+    // only finished s-1).  The slots are distinct arrays addressed statically, so
+    // the compiler can tell the reads of one slot from the copies in flight
+    // to the others.
     auto step = [&](const char *Kc, const char *Vp, char *Kn, char *Vn, int dprev, int dcur,
-                    const char *&src, int &dnext) {
+                    int &dnext) {
         // Hide the operand offsets from loop-invariant hoisting: otherwise
         // the compiler keeps a full set of addresses per slot live across
         // the loop and runs out of registers.  Recomputing them costs one
@@ -611,19 +612,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
             asm volatile("" : "+v"(vofs[q]));
         wait_vmcnt<BPW>();
         lds_barrier();
-        const char *const from = src;
-        auto dma = [&](int t) { issue_block<D>(plan, Kn, Vn, from, wave, t); };
         if (attends(dprev))
             pv_stage<D>(Vp, vofs, Pr, dprev & 255, st);
-        if (attends(dcur)) {
-            qk_stage<D>(S, Kc, qf, kofs, dcur & 255, hi, dma);
-        } else {
-#pragma unroll
-            for (int t = 0; t < BPW; ++t)
-                dma(t);
-        }
+        if (attends(dcur))
+            qk_stage<D>(S, Kc, qf, kofs, dcur & 255, hi, [](int) {});
         lds_barrier();
+        const char *src;
         dnext = take(src);
+#pragma unroll
+        for (int t = 0; t < BPW; ++t)
+            issue_block<D>(plan, Kn, Vn, src, wave, t);
         if (attends(dcur))
             softmax_stage<D>(Pr, S, dcur & 255, sl2, st, [](int) {});
         return dcur != 0;
@@ -631,21 +629,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     if (side == 1)
         lds_barrier();
     int dm1 = 0;
-    const char *src = src2;
     for (;;) {
-        int d3;
-        if (!step(K0, V3, K2, V2, dm1, d0, src, d3))
+        int d2;
+        if (!step(K0, V3, K2, V2, dm1, d0, d2))
             break;
-        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
-        if (!step(K1, V0, K3, V3, dm1, d0, src, d3))
+        dm1 = d0, d0 = d1, d1 = d2;
+        if (!step(K1, V0, K3, V3, dm1, d0, d2))
             break;
-        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
-        if (!step(K2, V1, K0, V0, dm1, d0, src, d3))
+        dm1 = d0, d0 = d1, d1 = d2;
+        if (!step(K2, V1, K0, V0, dm1, d0, d2))
             break;
-        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
-        if (!step(K3, V2, K1, V1, dm1, d0, src, d3))
+        dm1 = d0, d0 = d1, d1 = d2;
+        if (!step(K3, V2, K1, V1, dm1, d0, d2))
             break;
-        dm1 = d0, d0 = d1, d1 = d2, d2 = d3;
+        dm1 = d0, d0 = d1, d1 = d2;
     }
     if (side == 0)
         lds_barrier();  // pairs with B's extra barrier: both groups pass the same count

@@ -91,10 +91,16 @@ __host__ __device__ inline TilePair pair_tiles(const Layout &L, int pr)
     return r;
 }
 
-// Pair-list entries hold the key tile in the low 30 bits and, in bits 30 and
-// 31, whether the first and the second query tile of the pair keep it.
-constexpr int kPairShift = 30;
-constexpr int kPairTileMask = (1 << kPairShift) - 1;
+// A pair-list entry packs the key tile j (bits 0-15; the host keeps
+// nT <= 46340), its real token count c_j (bits 16-23, at most 128) and
+// whether the first and the second query tile of the pair keep it (bits 24
+// and 25).
+constexpr int kPairCountShift = 16;
+constexpr int kPairBitsShift = 24;
+__host__ __device__ inline int pair_entry(int j, int c, int bits)
+{
+    return j | (c << kPairCountShift) | (bits << kPairBitsShift);
+}
 
 // Division of 0 <= n < 2^31 by a fixed divisor 1 <= d < 2^31 with one
 // multiply-high, add and shift: the round-up method of Granlund and

@@ -24,7 +24,7 @@
 // The matrix-core attention kernel reads pair lists instead: the same stages
 // run over query-tile pairs r = h nP + pr (pair_tiles), keeping key tile j
 // when either tile of the pair keeps it, and each entry carries which of the
-// two does (j | bits << kPairShift).  The row lists stay the mask's
+// two does (pair_entry: j, its real token count, and the keep bits).  The row lists stay the mask's
 // definitive form (they are what the index-list hook returns).
 #include "common.h"
 
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void fill_kernel(Layout L, MaskBuffers mb,
         const unsigned long long bits = __ballot(kb != 0);
         const long long pos = base + __popcll(bits & below);
         if (kb && pos < mb.cap)
-            mb.cols[pos] = mb.pair ? (int)((unsigned)j | ((unsigned)kb << kPairShift)) : j;
+            mb.cols[pos] = mb.pair ? pair_entry(j, tile_real_count(L, j), kb) : j;
         base += __popcll(bits);
     }
 }

@@ -232,6 +232,8 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     L.nx = (L.W + L.tw - 1) / L.tw;
     const long long nT = (long long)L.nt * L.ny * L.nx;
     const long long N = (long long)L.T * L.H * L.W;
+    // This bound also keeps tile ids below 2^16, the width pair-list entries
+    // give them.
     if (nT * nT * c.heads >= (1ll << 31))
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED,
                     "heads * tiles^2 = %lld does not fit 32-bit index lists", nT * nT * c.heads);
