@@ -17,7 +17,8 @@ LIB = os.path.join(HERE, "libsparse_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sparse_attn.cpp", "permute.hip", "mask.hip", "attn_mfma.hip", "attn_generic.hip"]
+SOURCES = ["sparse_attn.cpp", "permute.hip", "mask.hip", "attn_mfma.hip", "attn_rows.hip",
+           "attn_generic.hip"]
 
 # Packed fp32 VALU instructions are switched off for every device compile.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
 
     const int tid = threadIdx.x;
     const int slot = tid >> 1, part = tid & 1;
-    const int r = P.order[blockIdx.x];
+    const int r = P.rows.order[blockIdx.x];
     const int h = r / L.nT, i = r - h * L.nT;
     const int ci = tile_real_count(L, i);
     const bool active = slot < L.B && slot < ci;
@@ -55,10 +55,10 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
     }
     float m = -INFINITY, l = 0.f;
 
-    const int beg = P.row_ptr[r];
-    const int end = (int)min((long long)P.row_ptr[r + 1], P.cap);
+    const int beg = P.rows.row_ptr[r];
+    const int end = (int)min((long long)P.rows.row_ptr[r + 1], P.rows.cap);
     for (int idx = beg; idx < end; ++idx) {
-        const int j = P.cols[idx];
+        const int j = P.rows.cols[idx];
         const int cj = tile_real_count(L, j);
         const long long krow0 = (long long)h * L.Npad + (long long)j * L.B;
         for (int k0 = 0; k0 < cj; k0 += kChunk) {

@@ -421,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     const uint16_t *__restrict__ Kp = (const uint16_t *)P.k;
     const uint16_t *__restrict__ Vt = (const uint16_t *)P.v;
     uint16_t *__restrict__ Op = (uint16_t *)P.o;
-    const int *__restrict__ cols = P.cols;
+    const int *__restrict__ cols = P.pairs.cols;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
@@ -441,7 +441,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
             w = ((slot / C) * 8 + xcd) * C + slot % C;
         }
     }
-    const int r = P.order[w];
+    const int r = P.pairs.order[w];
+    if (!P.pair_flag[r])
+        return;  // the row kernel serves these two tiles
     const int h = r / L.nP;
     const TilePair tp = pair_tiles(L, r - h * L.nP);
     const int i = side ? tp.t2 : tp.t1;
@@ -475,8 +477,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     st.l = 0.f;
     const float sl2 = P.scale_log2;
 
-    const int beg = P.row_ptr[r];
-    const int end = (int)min((long long)P.row_ptr[r + 1], P.cap);
+    const int beg = P.pairs.row_ptr[r];
+    const int end = (int)min((long long)P.pairs.row_ptr[r + 1], P.pairs.cap);
 
     // The pair's list entries, staged in LDS as a ring of two halves: entry
     // idx lives at clist[(idx - beg) % kList].  The first kList entries are

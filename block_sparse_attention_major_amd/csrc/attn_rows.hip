@@ -1,0 +1,427 @@
+// Block-sparse flash attention forward over single query tiles (the row
+// kernel), bf16 in / fp32 accumulate, on the gfx950 matrix cores
+// (v_mfma_f32_32x32x16_bf16).  It serves the query tiles whose pair the
+// mask compiler did not give to the pair kernel (attn_mfma.hip): pairs whose
+// two key lists overlap too little for a shared key stream to pay off, and
+// tiles left alone at an odd edge of the tile grid.
+//
+// What is computed: for every query tile i of head h, exact softmax
+// attention over the keys of the key tiles its mask row keeps (Compact
+// Attention page, Fig. 3 caption: precomputed masks run in block-sparse
+// attention kernels; SCOPE review page, abstract: attention over the selected
+// original keys and values).  Dropped tile pairs cost no loads and no FLOPs.
+//
+// Design (ours, for CDNA4; the pages give no kernel design):
+//  - One workgroup of 4 waves per (head, query tile); tile = 128 slots, each
+//    wave owns 32 query slots.  Two workgroups share a CU, so each SIMD runs
+//    two independent waves and overlaps one's softmax with the other's MFMAs.
+//    Workgroups follow the compiled longest-first order, remapped so each XCD
+//    (which owns its L2) takes contiguous chunks of it: neighbouring rows
+//    share key tiles.
+//  - Keys are consumed in stages of 64 (half a tile).  K and the transposed V
+//    tile of a stage are copied global -> LDS by the DMA path
+//    (global_load_lds_dwordx4: no registers, no LDS store instructions) into
+//    one of two statically addressed buffers, one stage ahead of the math.
+//    The empty tail of a clipped key tile (80 of 128 slots at 720p) is
+//    skipped at 32-key granularity.
+//  - Scores are computed transposed, S^T = K Q^T, so each lane holds 16 keys
+//    of one query: row max and row sum are in-lane, plus one exchange with
+//    the lane 32 apart (v_permlane32_swap).  K rows are fed to the MFMA in a
+//    permuted order so the probabilities come out already in the operand
+//    order of the next product, O^T += V^T P^T, whose accumulator again keeps
+//    one query per lane (the rescale is in-lane).
+//  - V arrives pre-transposed per tile ([D][128], written by the permute
+//    stage), so V^T operand reads are plain 16-byte LDS reads.
+//  - LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
+//    16 distinct chunk positions per 16 lanes.
+//  - Online softmax in fp32 and exp2 with a lazily moved running max; row
+//    sums are taken from the bf16 probabilities with v_dot2.
+#include "common.h"
+
+namespace sa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr int kThreads = 256;
+constexpr int kTile = 128;   // slots per tile
+constexpr int kStage = 64;   // keys per LDS stage
+constexpr int kList = 2048;  // key-tile ids staged in LDS at a time
+
+// Probabilities are kept below 2^kLazy (see the online softmax below).
+constexpr float kLazy = 8.0f;
+
+// Byte offset of 16-byte chunk c of row `row` in an LDS block whose rows hold
+// RC chunks.  Rows are packed into 256-byte lines; the chunk index is XORed
+// with the line index so 16 consecutive rows read at one column hit 16
+// different chunk positions.
+template <int RC>
+__device__ __forceinline__ int lds_off(int row, int c)
+{
+    constexpr int RPL = 16 / RC;
+    const int line = row / RPL;
+    const int logical = (row % RPL) * RC + c;
+    return line * 256 + ((logical ^ (line & 15)) << 4);
+}
+
+// Key row fed to MFMA row m of a 32-key subtile.  With this order, result
+// register j of lane l holds key 16 (j / 8) + 8 (l / 32) + j % 8, which is
+// the B-operand order of the P V^T product.
+__device__ __forceinline__ int key_of_mfma_row(int m)
+{
+    const int a = m >> 3, b = (m >> 2) & 1, c = m & 3;
+    return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Lanes l and l ^ 32 hold the two halves of one query row.
+__device__ __forceinline__ float half_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// acc + sum of the 8 bf16 values of p (two per v_dot2 with a vector of ones).
+__device__ __forceinline__ float row_sum_bf16(bf16x8 p, float acc)
+{
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+}
+
+// Real tokens of tile j (clipped at the far edges of the grid).
+__device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P, int j)
+{
+    const int a = (int)fast_div((uint32_t)j, P.div_plane);
+    const int rem = j - a * L.ny * L.nx;
+    const int b = (int)fast_div((uint32_t)rem, P.div_row);
+    const int e = rem - b * L.nx;
+    return min(L.tt, L.T - a * L.tt) * min(L.th, L.H - b * L.th) * min(L.tw, L.W - e * L.tw);
+}
+
+// One stage (64 keys, half `half` of key tile j) in LDS: K rows [64][D] then
+// transposed V [D][64], both swizzled.  The stage is 2 * D KB, moved as 1 KB
+// DMA blocks of 64 lanes x 16 bytes; LDS byte 16 l of a block receives lane
+// l's load, so each lane fetches the global chunk that the swizzle puts
+// there.  Wave w issues blocks [w * BPW, (w + 1) * BPW).
+template <int D>
+__device__ __forceinline__ void issue_stage(lds_char *stage, const uint16_t *__restrict__ Kp,
+                                            const uint16_t *__restrict__ Vt, const Layout &L, int h,
+                                            int j, int half, int wave, int lane)
+{
+    constexpr int RCK = D / 8;                   // 16-byte chunks per K row
+    constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
+    constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
+    // Uniform bases of the stage in the permuted K and transposed V.
+    const char *kbase = (const char *)(Kp + ((long long)h * L.Npad + (long long)j * kTile + half * kStage) * D);
+    const char *vbase = (const char *)(Vt + ((long long)h * L.nT + j) * D * kTile + half * kStage);
+    const int line_in_blk = lane >> 4, phys = lane & 15;
+#pragma unroll
+    for (int t = 0; t < BPW; ++t) {
+        const int blk = wave * BPW + t;  // wave-uniform
+        const int kb = blk < KBLK ? blk : blk - KBLK;
+        const int line = 4 * kb + line_in_blk;
+        const int logical = phys ^ (line & 15);
+        const char *src;
+        if (blk < KBLK) {
+            constexpr int RPL = 16 / RCK;
+            const int row = RPL * line + logical / RCK, c = logical % RCK;
+            src = kbase + (row * D * 2 + 16 * c);
+        } else {
+            const int dv = 2 * line + (logical >> 3), c = logical & 7;
+            src = vbase + (dv * kTile * 2 + 16 * c);
+        }
+        __builtin_amdgcn_global_load_lds((const void *)src,
+                                         (void __attribute__((address_space(3))) *)(stage + blk * 1024),
+                                         16, 0, 0);
+    }
+}
+
+// The per-wave state of one query block: 32 queries x D features.
+template <int D>
+struct RowState {
+    f32x16 acc[D / 32];
+    float m, l;  // running max (log2 units) and partial row sum of this lane
+};
+
+// Attention of this wave's 32 queries to the kv real keys (1..64) of the
+// stage held in LDS at Ks (K) and Ks + K_BYTES (V^T).
+template <int D>
+__device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[D / 16], int kv,
+                                             float sl2, int prow, int l32, int hi, RowState<D> &st)
+{
+    constexpr int KS = D / 16, NB = D / 32, RCK = D / 8;
+    constexpr int K_BYTES = kStage * D * 2;
+    const char *Vs = Ks + K_BYTES;
+    const bool two = kv > 32;
+    f32x16 s0, s1;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        s0[jj] = 0.f;
+        s1[jj] = 0.f;
+    }
+    if (two) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi));
+            const bf16x8 a1 = *(const bf16x8 *)(Ks + lds_off<RCK>(32 + prow, 2 * ks + hi));
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], s1, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi)), qf[ks], s0, 0, 0, 0);
+    }
+    if (kv < kStage) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            const int key = 16 * (jj >> 3) + 8 * hi + (jj & 7);
+            if (key >= kv)
+                s0[jj] = -INFINITY;
+            if (32 + key >= kv)
+                s1[jj] = -INFINITY;
+        }
+    }
+    float mx = s0[0];
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj)
+        mx = fmaxf(mx, s0[jj]);
+    if (two) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            mx = fmaxf(mx, s1[jj]);
+    }
+    // Running max in log2 units, moved lazily: only when some row's new
+    // maximum exceeds it by more than kLazy, so the rescale of the
+    // accumulator is a rare wave-uniform branch.  Numerator and denominator
+    // share the max, so the result does not depend on it; probabilities stay
+    // below 2^kLazy.
+    const float t = half_max(mx) * sl2;
+    if (__ballot(t > st.m + kLazy)) {
+        const float m_new = fmaxf(st.m, t);
+        const float alpha = exp2_fast(st.m - m_new);
+        st.m = m_new;
+        st.l *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                st.acc[nb][jj] *= alpha;
+    }
+    bf16x8 p0a, p0b, p1a, p1b;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+        p0a[jj] = (__bf16)exp2_fast(fmaf(s0[jj], sl2, -st.m));
+        p0b[jj] = (__bf16)exp2_fast(fmaf(s0[jj + 8], sl2, -st.m));
+    }
+    st.l = row_sum_bf16(p0a, row_sum_bf16(p0b, st.l));
+    if (two) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+            p1a[jj] = (__bf16)exp2_fast(fmaf(s1[jj], sl2, -st.m));
+            p1b[jj] = (__bf16)exp2_fast(fmaf(s1[jj + 8], sl2, -st.m));
+        }
+        st.l = row_sum_bf16(p1a, row_sum_bf16(p1b, st.l));
+    }
+    // O^T += V^T P^T: A operand = V^T rows 32 nb + l32, keys in 16-key steps.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 0 + hi)), p0a, st.acc[nb], 0, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 2 + hi)), p0b, st.acc[nb], 0, 0, 0);
+    if (two) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 4 + hi)), p1a, st.acc[nb], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 6 + hi)), p1b, st.acc[nb], 0, 0, 0);
+    }
+}
+
+// Wait for this wave's outstanding vector-memory operations (the stage DMA),
+// leaving LDS and scalar counters alone.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnParams P)
+{
+    constexpr int KS = D / 16;
+    constexpr int NB = D / 32;
+    constexpr int STAGE_BYTES = 2 * kStage * D * 2;
+    __shared__ __attribute__((aligned(1024))) char buf0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char buf1[STAGE_BYTES];
+    __shared__ int clist[kList];
+
+    const uint16_t *__restrict__ Qp = (const uint16_t *)P.q;
+    const uint16_t *__restrict__ Kp = (const uint16_t *)P.k;
+    const uint16_t *__restrict__ Vt = (const uint16_t *)P.v;
+    uint16_t *__restrict__ Op = (uint16_t *)P.o;
+    const int *__restrict__ cols = P.rows.cols;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int l32 = lane & 31, hi = lane >> 5;
+
+    // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD
+    // contiguous chunks of the work order.
+    int w = blockIdx.x;
+    {
+        const int C = P.xcd_chunk;
+        const int G = gridDim.x;
+        const int G8 = C > 0 ? (G / (8 * C)) * (8 * C) : 0;
+        if (w < G8) {
+            const int xcd = w & 7, slot = w >> 3;
+            w = ((slot / C) * 8 + xcd) * C + slot % C;
+        }
+    }
+    const int r = P.rows.order[w];
+    const int h = r / L.nT, i = r - h * L.nT;
+    if (P.pair_flag[h * L.nP + tile_pair(L, i)])
+        return;  // the pair kernel serves this tile
+    const int ci = tile_tokens(L, P, i);
+    const bool wave_active = wave * 32 < ci;
+
+    // Q operand (B of S^T = K Q^T): lane holds query l32, features
+    // 16 ks + 8 hi .. +7 for every k-step.
+    const long long qrow = (long long)h * L.Npad + (long long)i * kTile + wave * 32 + l32;
+    bf16x8 qf[KS];
+    {
+        const bf16x8 *qp = (const bf16x8 *)(Qp + qrow * D);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = qp[2 * ks + hi];
+    }
+    RowState<D> st;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            st.acc[nb][jj] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    const float sl2 = P.scale_log2;
+
+    const int beg = P.rows.row_ptr[r];
+    const int end = (int)min((long long)P.rows.row_ptr[r + 1], P.rows.cap);
+
+    // The row's key-tile ids, staged in LDS (kList at a time; longer rows
+    // refill the list when the cursor reaches its end).
+    int list_base = beg, list_end = beg;
+    auto fill_list = [&](int from) {
+        list_base = from;
+        list_end = min(end, from + kList);
+        for (int u = tid; u < list_end - list_base; u += kThreads)
+            clist[u] = cols[list_base + u];
+        __syncthreads();
+    };
+
+    // Stage cursor: key tile idx (id j, c real tokens) and which half of it.
+    int idx = beg, half = 0, j = 0, c = 0;
+    if (idx < end) {
+        fill_list(beg);
+        j = clist[0];
+        c = tile_tokens(L, P, j);
+        issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, 0, wave, lane);
+    }
+    const int prow = key_of_mfma_row(l32);
+
+    // Advance the cursor by one stage (all waves together, after a barrier).
+    auto advance = [&]() {
+        if (half == 0 && c > kStage) {
+            half = 1;
+        } else {
+            ++idx;
+            half = 0;
+            if (idx < end) {
+                if (idx == list_end) {
+                    __syncthreads();  // every wave is done reading the list
+                    fill_list(idx);
+                }
+                j = clist[idx - list_base];
+                c = tile_tokens(L, P, j);
+            }
+        }
+    };
+
+    while (idx < end) {
+        // ---- stage in buf0
+        {
+            const int kv = min(kStage, c - half * kStage);
+            wait_vmem();
+            __syncthreads();  // buf0 complete; buf1 free
+            advance();
+            if (idx < end)
+                issue_stage<D>((lds_char *)buf1, Kp, Vt, L, h, j, half, wave, lane);
+            if (wave_active)
+                attend_stage<D>(buf0, qf, kv, sl2, prow, l32, hi, st);
+        }
+        if (idx >= end)
+            break;
+        // ---- stage in buf1
+        {
+            const int kv = min(kStage, c - half * kStage);
+            wait_vmem();
+            __syncthreads();  // buf1 complete; buf0 free
+            advance();
+            if (idx < end)
+                issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, half, wave, lane);
+            if (wave_active)
+                attend_stage<D>(buf1, qf, kv, sl2, prow, l32, hi, st);
+        }
+    }
+
+    if (wave_active) {
+        const float lt = half_sum(st.l);
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t *orow = Op + qrow * D;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                // O^T accumulator register 4 g + u of lane l holds feature
+                // 32 nb + 8 g + 4 hi + u of query l32.
+                union {
+                    __bf16 b[4];
+                    uint2 u;
+                } pk;
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    pk.b[u] = (__bf16)(st.acc[nb][4 * g + u] * inv);
+                *(uint2 *)(orow + 32 * nb + 8 * g + 4 * hi) = pk.u;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attention_rows(const Layout &L, const AttnParams &p, hipStream_t s)
+{
+    const dim3 grid(L.heads * L.nT);
+    if (L.D == 128)
+        hipLaunchKernelGGL(attn_rows_kernel<128>, grid, dim3(kThreads), 0, s, L, p);
+    else
+        hipLaunchKernelGGL(attn_rows_kernel<64>, grid, dim3(kThreads), 0, s, L, p);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -65,6 +65,21 @@ struct TilePair {
     int t1, t2;
 };
 
+// The pair holding query tile i (inverse of pair_tiles).
+__host__ __device__ inline int tile_pair(const Layout &L, int i)
+{
+    int a = i / (L.ny * L.nx);
+    int b = (i / L.nx) % L.ny;
+    int e = i % L.nx;
+    if (L.pax == 0)
+        a >>= 1;
+    else if (L.pax == 1)
+        b >>= 1;
+    else if (L.pax == 2)
+        e >>= 1;
+    return (a * L.pn[1] + b) * L.pn[2] + e;
+}
+
 __host__ __device__ inline TilePair pair_tiles(const Layout &L, int pr)
 {
     int a = pr / (L.pn[1] * L.pn[2]);
@@ -154,7 +169,16 @@ struct MaskBuffers {
     int R;
     int nchunks;
     int pair;       // 0: rows r = h nT + i; 1: pairs r = h nP + pr (entries carry keep bits)
+    int *flag;      // pairs only, [R]: 1 = the pair kernel serves the pair (see kPairNum)
 };
+
+// A pair of query tiles goes to the pair kernel when the union of their key
+// lists is at most kPairNum / kPairDen of the two lists' total length (every
+// kept key tile of the union is then loaded once for both tiles often enough
+// to pay for the steps where only one tile computes); otherwise both tiles
+// go to the row kernel.  A pair with no kept tiles is served by the pair
+// kernel (it writes zeros).
+constexpr int kPairNum = 7, kPairDen = 10;
 
 constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
 
@@ -163,23 +187,32 @@ constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
 hipError_t launch_compile_mask(const Layout &L, int kind, const uint8_t *bitmap,
                                const MaskBuffers &mb, const MaskBuffers &pb, hipStream_t s);
 
+// One compiled set of index lists.
+struct ListSet {
+    const int *row_ptr;
+    const int *cols;
+    const int *order;
+    long long cap;      // valid entries of cols
+};
+
 struct AttnParams {
     const void *q;      // tile-major rows
     const void *k;      // tile-major rows
     const void *v;      // tile-major rows (generic) or tile columns (MFMA)
     void *o;            // tile-major rows
-    const int *row_ptr; // generic kernel: rows; matrix-core kernel: pairs
-    const int *cols;
-    const int *order;
-    long long cap;      // valid entries of cols
+    ListSet rows;       // per query tile
+    ListSet pairs;      // per query-tile pair (matrix-core kernels only)
+    const int *pair_flag;  // [heads nP] (matrix-core kernels only)
     float scale_log2;   // softmax scale * log2(e)
     int xcd_chunk;      // rows per XCD chunk of the work order (0: plain order)
     FastDiv div_plane;  // ny * nx: tiles per tile-grid plane
     FastDiv div_row;    // nx: tiles per tile-grid row
 };
 
-// bf16 matrix-core kernel over query-tile pairs: B == 128, D in {64, 128}.
+// bf16 matrix-core kernels, B == 128, D in {64, 128}: the pair kernel over
+// accepted query-tile pairs, then the row kernel over the other query tiles.
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
+hipError_t launch_attention_rows(const Layout &L, const AttnParams &p, hipStream_t s);
 // fp32 vector-ALU kernel for any supported shape; elem_bytes 4 (fp32) or 2 (bf16).
 hipError_t launch_attention_generic(const Layout &L, int elem_bytes, const AttnParams &p,
                                     hipStream_t s);

@@ -21,11 +21,14 @@
 //   fill   : one wave per row -> ascending key-tile ids
 //   order  : one workgroup per chunk -> order[base + rank among equal lengths]
 //
-// The matrix-core attention kernel reads pair lists instead: the same stages
-// run over query-tile pairs r = h nP + pr (pair_tiles), keeping key tile j
-// when either tile of the pair keeps it, and each entry carries which of the
-// two does (pair_entry: j, its real token count, and the keep bits).  The row lists stay the mask's
-// definitive form (they are what the index-list hook returns).
+// The matrix-core path also gets pair lists: the same stages run over
+// query-tile pairs r = h nP + pr (pair_tiles), keeping key tile j when
+// either tile of the pair keeps it, and each entry carries which of the two
+// does (pair_entry: j, its real token count, and the keep bits).  The count
+// stage also decides, per pair, whether the pair kernel serves it (flag;
+// see kPairNum); a pair it does not serve gets an empty list.  The row
+// lists stay the mask's definitive form (they are what the index-list hook
+// returns).
 #include "common.h"
 
 namespace sa {
@@ -130,12 +133,26 @@ __global__ __launch_bounds__(256) void count_kernel(Layout L, MaskBuffers mb,
         return;
     const int lane = threadIdx.x & 63;
     const ListRow q = list_row(L, mb, r);
-    int n = 0;
-    for (int j = lane; j < L.nT; j += kWave)
-        n += keep_bits<KIND>(L, mb, bitmap, q, j) ? 1 : 0;
+    // n: list length (union for a pair); n12: kept entries of each tile
+    // summed (a pair's two row lengths).
+    int n = 0, n12 = 0;
+    for (int j = lane; j < L.nT; j += kWave) {
+        const int kb = keep_bits<KIND>(L, mb, bitmap, q, j);
+        n += kb ? 1 : 0;
+        n12 += (kb & 1) + (kb >> 1);
+    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
+    for (int off = 32; off > 0; off >>= 1) {
         n += __shfl_xor(n, off);
+        n12 += __shfl_xor(n12, off);
+    }
+    if (mb.pair) {
+        const int accept = (long long)n * kPairDen <= (long long)kPairNum * n12 ? 1 : 0;
+        if (lane == 0)
+            mb.flag[r] = accept;
+        if (!accept)
+            n = 0;  // the row kernel serves both tiles
+    }
     if (lane == 0) {
         mb.len[r] = n;
         atomicAdd(&mb.chunk[(long long)(r / kMaskChunk) * (L.nT + 1) + n], 1);
@@ -218,6 +235,8 @@ __global__ __launch_bounds__(256) void fill_kernel(Layout L, MaskBuffers mb,
     const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= mb.R)
         return;
+    if (mb.pair && !mb.flag[r])
+        return;  // no list: the row kernel serves both tiles
     const int lane = threadIdx.x & 63;
     const ListRow q = list_row(L, mb, r);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));

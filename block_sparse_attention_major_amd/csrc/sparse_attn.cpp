@@ -65,7 +65,7 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 // merges, so cap entries hold it whenever they hold the rows.
 struct MaskLayout {
     size_t row_ptr, len, order, chunk, bucket, status, groups, group_off;
-    size_t p_row_ptr, p_len, p_order, p_chunk, p_bucket;
+    size_t p_row_ptr, p_len, p_order, p_chunk, p_bucket, p_flag;
     size_t cols;  // start of the index lists
     int R, nchunks, P, pnchunks;
 };
@@ -97,6 +97,7 @@ MaskLayout mask_layout(const sa::Layout &L, bool pairs)
         m.p_order = take(4 * size_t(m.P));
         m.p_chunk = take(4 * size_t(m.pnchunks) * size_t(L.nT + 1));
         m.p_bucket = take(4 * size_t(L.nT + 1));
+        m.p_flag = take(4 * size_t(m.P));
     }
     m.cols = off;
     return m;
@@ -159,11 +160,9 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     p.k = b + w.k;
     p.v = b + w.v;
     p.o = b + w.o;
-    const sa::MaskBuffers &lists = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? h->pb : h->mb;
-    p.row_ptr = lists.row_ptr;
-    p.cols = lists.cols;
-    p.order = lists.order;
-    p.cap = lists.cap;
+    p.rows = sa::ListSet{h->mb.row_ptr, h->mb.cols, h->mb.order, h->mb.cap};
+    p.pairs = sa::ListSet{h->pb.row_ptr, h->pb.cols, h->pb.order, h->pb.cap};
+    p.pair_flag = h->pb.flag;
     p.scale_log2 = h->scale * 1.4426950408889634f;
     // Consecutive work items of one XCD take 32 consecutive (longest-first)
     // rows, so query tiles that share key tiles share that XCD's L2.
@@ -391,6 +390,7 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
     mb.R = ml.R;
     mb.nchunks = ml.nchunks;
     mb.pair = 0;
+    mb.flag = nullptr;
     sa::MaskBuffers pb{};
     if (pairs) {
         pb = mb;
@@ -404,6 +404,7 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
         pb.R = ml.P;
         pb.nchunks = ml.pnchunks;
         pb.pair = 1;
+        pb.flag = reinterpret_cast<int *>(base + ml.p_flag);
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -468,9 +469,14 @@ int sparse_attn_attend(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *s
         return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before attention");
     const sa::AttnParams p = attn_params(h, ws);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16
-                             ? sa::launch_attention_mfma(h->L, p, s)
-                             : sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
+    hipError_t e;
+    if (h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16) {
+        e = sa::launch_attention_mfma(h->L, p, s);
+        if (e == hipSuccess)
+            e = sa::launch_attention_rows(h->L, p, s);
+    } else {
+        e = sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
+    }
     if (e != hipSuccess)
         return hip_fail(h, e, "attention launch");
     return SPARSE_ATTN_OK;
