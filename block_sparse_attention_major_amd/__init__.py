@@ -50,6 +50,7 @@ EXPORTED = [
     "sparse_attn_workspace_bytes", "sparse_attn_set_mask", "sparse_attn_forward",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
+    "sparse_attn_read_pair_lists",
     "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
 ]
 
@@ -77,7 +78,8 @@ class sparse_attn_layout_info(ctypes.Structure):
                 ("slots", ctypes.c_int64), ("kernel", ctypes.c_int32), ("v_layout", ctypes.c_int32),
                 ("ws_offset_q", ctypes.c_size_t), ("ws_offset_k", ctypes.c_size_t),
                 ("ws_offset_v", ctypes.c_size_t), ("ws_offset_o", ctypes.c_size_t),
-                ("ws_bytes", ctypes.c_size_t)]
+                ("ws_bytes", ctypes.c_size_t), ("pair_axis", ctypes.c_int32),
+                ("pair_grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int64)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -96,6 +98,7 @@ _sigs = {
     "sparse_attn_permute": ([_vp, _vp, _vp, _i32, _vp], ctypes.c_int),
     "sparse_attn_unpermute": ([_vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_read_index_lists": ([_vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
+    "sparse_attn_read_pair_lists": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_mask_info": ([_vp, _P(_i64), _P(_i32), _vp], ctypes.c_int),
     "sparse_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sparse_attn_last_error": ([_vp], ctypes.c_char_p),
@@ -187,7 +190,7 @@ def sparse_attn_destroy(h):
 def sparse_attn_layout(h):
     info = sparse_attn_layout_info()
     _check(_lib.sparse_attn_layout(h.ptr, ctypes.byref(info)), h)
-    return {f: (list(getattr(info, f)) if f == "tile_grid" else getattr(info, f))
+    return {f: (list(getattr(info, f)) if f in ("tile_grid", "pair_grid") else getattr(info, f))
             for f, _ in sparse_attn_layout_info._fields_}
 
 
@@ -258,6 +261,13 @@ def sparse_attn_read_index_lists(h, row_ptr, cols, order, stream=None):
     _check(_lib.sparse_attn_read_index_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
                                              cols.numel() if cols is not None else 0,
                                              _dptr(order, "order"), _stream(stream)), h)
+
+
+def sparse_attn_read_pair_lists(h, row_ptr, cols, order, flag, stream=None):
+    _check(_lib.sparse_attn_read_pair_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
+                                            cols.numel() if cols is not None else 0,
+                                            _dptr(order, "order"), _dptr(flag, "flag"),
+                                            _stream(stream)), h)
 
 
 def sparse_attn_mask_info(h, stream=None):

@@ -292,6 +292,10 @@ int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *inf
     info->ws_offset_v = w.v;
     info->ws_offset_o = w.o;
     info->ws_bytes = w.total;
+    info->pair_axis = h->L.pax;
+    for (int a = 0; a < 3; ++a)
+        info->pair_grid[a] = h->L.pn[a];
+    info->pairs = h->L.nP;
     return SPARSE_ATTN_OK;
 }
 
@@ -580,6 +584,32 @@ int sparse_attn_read_index_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_
         e = hipMemcpyAsync(cols, h->mb.cols, 4 * size_t(n), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess)
         return hip_fail(h, e, "copying index lists");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_read_pair_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t *cols,
+                                int64_t cols_capacity, int32_t *order, int32_t *flag, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (!row_ptr || !order || !flag || (!cols && cols_capacity > 0) || cols_capacity < 0)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "null destination");
+    if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "pair lists exist for the matrix-core kernel only");
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "no mask set");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int P = h->pb.R;
+    hipError_t e = hipMemcpyAsync(row_ptr, h->pb.row_ptr, 4 * size_t(P + 1), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(order, h->pb.order, 4 * size_t(P), hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(flag, h->pb.flag, 4 * size_t(P), hipMemcpyDeviceToDevice, s);
+    const long long n = std::min<long long>(cols_capacity, h->pb.cap);
+    if (e == hipSuccess && n > 0)
+        e = hipMemcpyAsync(cols, h->pb.cols, 4 * size_t(n), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "copying pair lists");
     return SPARSE_ATTN_OK;
 }
 

@@ -136,6 +136,13 @@ typedef struct sparse_attn_layout_info {
     /* Byte offsets of the permuted Q, K, V and of the tile-major output O
      * inside the forward workspace, and the workspace size. */
     size_t ws_offset_q, ws_offset_k, ws_offset_v, ws_offset_o, ws_bytes;
+    /* Query-tile pairs of the matrix-core kernel: tiles (2c, 2c + 1) along
+     * tile-grid axis pair_axis (0 = t, 1 = y, 2 = x; -1: none) form pair
+     * c, numbered raster over pair_grid (the tile grid with that axis halved,
+     * rounded up); pairs is pairs per head. */
+    int32_t pair_axis;
+    int32_t pair_grid[3];
+    int64_t pairs;
 } sparse_attn_layout_info;
 
 typedef struct sparse_attn_handle sparse_attn_handle;
@@ -215,15 +222,24 @@ int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_byte
  * sparse_attn_read_index_lists: copy the compiled row offsets (int32
  *   [heads nT + 1]), index list (int32, first min(nnz, cols_capacity)
  *   entries) and work order (int32 [heads nT]) into device buffers.
+ * sparse_attn_read_pair_lists: the same for the query-tile pair lists of
+ *   the matrix-core kernel (rows r = h * pairs + p), plus flag (int32
+ *   [heads * pairs]: 1 when the pair kernel serves the pair, whose list is
+ *   then the union of its two tiles' rows; 0 when the row kernel serves its
+ *   tiles and its list is empty).  Each entry packs key tile j (bits 0-15),
+ *   its real token count (bits 16-23) and whether the pair's first and
+ *   second tile keep it (bits 24, 25).  UNSUPPORTED for the generic kernel.
  * sparse_attn_mask_info: synchronizes `stream`, then reports the number of
  *   kept pairs and whether the index list overflowed its capacity.
- * Errors: INVALID_ARG, NO_MASK (index lists), HIP_ERROR.
+ * Errors: INVALID_ARG, NO_MASK (index lists), UNSUPPORTED, HIP_ERROR.
  */
 int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32_t layout,
                         void *stream);
 int sparse_attn_unpermute(sparse_attn_handle *h, const void *src, void *dst, void *stream);
 int sparse_attn_read_index_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t *cols,
                                  int64_t cols_capacity, int32_t *order, void *stream);
+int sparse_attn_read_pair_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t *cols,
+                                int64_t cols_capacity, int32_t *order, int32_t *flag, void *stream);
 int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow, void *stream);
 
 /* Static description of a status code. */

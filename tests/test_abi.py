@@ -69,6 +69,21 @@ def test_create_and_layout(sa):
     assert sa.sparse_attn_mask_bytes(tiny, 100) == full - 4 * (2 * 16 * 16 - 100)
 
 
+@pytest.mark.parametrize("grid,axis,pgrid", [
+    ((21, 45, 80), 1, [21, 3, 5]),   # tile grid 21 x 6 x 5: y even
+    ((4, 24, 32), 0, [2, 3, 2]),     # 4 x 3 x 2: y odd, t even
+    ((3, 24, 64), 2, [3, 3, 2]),     # 3 x 3 x 4: only x even
+    ((3, 40, 48), 1, [3, 3, 3]),     # 3 x 5 x 3: all odd -> y, last tile row alone
+    ((1, 8, 16), -1, [1, 1, 1]),     # one tile: no pairing
+])
+def test_pair_axis_choice(sa, grid, axis, pgrid):
+    h = sa.sparse_attn_create(2, 128, grid, (1, 8, 16), "bf16")
+    L = sa.sparse_attn_layout(h)
+    assert L["pair_axis"] == axis and L["pair_grid"] == pgrid
+    assert L["pairs"] == pgrid[0] * pgrid[1] * pgrid[2]
+    sa.sparse_attn_destroy(h)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(heads=0), 1), (dict(grid=(0, 8, 8)), 1), (dict(tile=(1, 0, 4)), 1),
     (dict(dtype=7), 1), (dict(softmax_scale=-1.0), 1), (dict(softmax_scale=float("inf")), 1),
