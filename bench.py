@@ -40,12 +40,20 @@ WORKLOAD_NAMES = {
     "small": "small video: 12 heads x 9,600 tokens, d=128, tile 1x8x16, dual-window masks",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_wan_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_attention_major_amd", "csrc", "attn_mfma.hip")
+# The attention stage's two kernels, and the files that decide their work
+# split and layout; counter results taken on other versions of these are
+# not reported.
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_major_amd", "csrc", f)
+                  for f in ("attn_mfma.hip", "attn_rows.hip", "mask.hip", "common.h")]
+ATTN_KERNELS = "attn_mfma_kernel<128> (query-tile pairs) + attn_rows_kernel<128> (single tiles)"
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_per_launch(workload):
@@ -225,7 +233,7 @@ def main():
                    "tile_density": round(info["tile_density"], 5),
                    "token_density": round(info["token_density"], 5),
                    "step": "mask compile + permute + block-sparse attention + unpermute"},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel<128>", "achieved": attn_tflops,
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F},
         "attention": {"ms": attn_ms, "ms_min": float(attn_min), "tflops": attn_tflops,
