@@ -45,6 +45,11 @@ def _load():
         lib.oracle_probabilities.argtypes = [g, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
                                              ctypes.c_void_p]
+        lib.oracle_tile_means.argtypes = [g, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+        lib.oracle_select_topk.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -160,6 +165,35 @@ def probabilities(grid, tile, q, k, Mh, scale=None):
     _load().oracle_probabilities(ctypes.byref(_grid(grid, tile)), d, _dtype_code(q), _ptr(q), _ptr(k),
                                  _ptr(np.ascontiguousarray(Mh, dtype=np.uint8)), float(scale), _ptr(P))
     return P
+
+
+def tile_means(grid, tile, x):
+    """fp64 mean of each tile's real tokens: x [N, d] -> [nT, d]."""
+    x = np.ascontiguousarray(x)
+    N, d = x.shape
+    out = np.empty((num_tiles(grid, tile), d), dtype=np.float64)
+    _load().oracle_tile_means(ctypes.byref(_grid(grid, tile)), d, _dtype_code(x), _ptr(x), _ptr(out))
+    return out
+
+
+def select_topk(grid, tile, q, k, kh, scale=None, threads=None):
+    """Tile mask [heads, nT, nT]: row i of head h keeps the kh[h] key tiles
+    with the largest mean-pooled score scale * qbar_i . kbar_j, ties to the
+    lower j."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    heads, N, d = q.shape
+    if _dtype_code(k) != _dtype_code(q):
+        raise TypeError("q, k must share a dtype")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nT = num_tiles(grid, tile)
+    kh = np.ascontiguousarray(kh, dtype=np.int64)
+    M = np.empty((heads, nT, nT), dtype=np.uint8)
+    _load().oracle_select_topk(ctypes.byref(_grid(grid, tile)), heads, d, _dtype_code(q), _ptr(q),
+                               _ptr(k), _ptr(kh), float(scale), _ptr(M),
+                               int(threads or default_threads()))
+    return M
 
 
 def flops(M, counts, d):

@@ -320,3 +320,83 @@ void oracle_probabilities(const oracle_grid *g, int64_t d, int dtype, const void
                 P[n * N + m] /= den;
     }
 }
+
+/*
+ * Tile selection by block-level proxy scores (SCOPE review page: the
+ * abstract names masks built from block-level proxy scores, "The reading"
+ * a per-head Top-k count, "What carries the argument" the 1/sqrt(d) scale of
+ * a proxy logit; AdaSpa page, abstract: a blockified pattern).  The reading
+ * used here, the plainest block-level proxy: the score of tile pair (i, j)
+ * is scale * qbar_i . kbar_j with qbar, kbar the means of the tiles' real
+ * tokens, and row i of head h keeps the k_h tiles with the largest score,
+ * ties to the lower j.
+ */
+
+/* Mean of each tile's real tokens: x [N][d] of the given dtype -> out [nT][d]. */
+void oracle_tile_means(const oracle_grid *g, int64_t d, int dtype, const void *x, double *out)
+{
+    int64_t N = g->T * g->H * g->W;
+    int64_t nT = oracle_num_tiles(g);
+    int64_t *cnt = calloc((size_t)nT, sizeof *cnt);
+    memset(out, 0, (size_t)(nT * d) * sizeof *out);
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t t = tile_of_token(g, n);
+        cnt[t] += 1;
+        for (int64_t e = 0; e < d; ++e)
+            out[t * d + e] += load_elem(x, dtype, n * d + e);
+    }
+    for (int64_t t = 0; t < nT; ++t)
+        for (int64_t e = 0; e < d; ++e)
+            out[t * d + e] = cnt[t] ? out[t * d + e] / (double)cnt[t] : 0.0;
+    free(cnt);
+}
+
+typedef struct {
+    double score;
+    int64_t j;
+} scored_tile;
+
+/* Larger score first, then lower tile id. */
+static int cmp_score(const void *pa, const void *pb)
+{
+    const scored_tile *a = pa, *b = pb;
+    if (a->score != b->score)
+        return a->score > b->score ? -1 : 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+/*
+ * q, k: [heads][N][d]; kh[heads] in 0..nT; M: [heads][nT][nT] (0/1) out.
+ */
+void oracle_select_topk(const oracle_grid *g, int64_t heads, int64_t d, int dtype, const void *q,
+                        const void *k, const int64_t *kh, double scale, uint8_t *M, int nthreads)
+{
+    int64_t N = g->T * g->H * g->W;
+    int64_t nT = oracle_num_tiles(g);
+    size_t esz = dtype == 0 ? 4 : 2;
+    double *qb = malloc((size_t)(nT * d) * sizeof *qb);
+    double *kb = malloc((size_t)(nT * d) * sizeof *kb);
+    for (int64_t h = 0; h < heads; ++h) {
+        oracle_tile_means(g, d, dtype, (const char *)q + (size_t)(h * N * d) * esz, qb);
+        oracle_tile_means(g, d, dtype, (const char *)k + (size_t)(h * N * d) * esz, kb);
+#pragma omp parallel for schedule(dynamic, 8) num_threads(nthreads)
+        for (int64_t i = 0; i < nT; ++i) {
+            scored_tile *row = malloc((size_t)nT * sizeof *row);
+            for (int64_t j = 0; j < nT; ++j) {
+                double dot = 0.0;
+                for (int64_t e = 0; e < d; ++e)
+                    dot += qb[i * d + e] * kb[j * d + e];
+                row[j].score = scale * dot;
+                row[j].j = j;
+            }
+            qsort(row, (size_t)nT, sizeof *row, cmp_score);
+            uint8_t *Mrow = M + (h * nT + i) * nT;
+            memset(Mrow, 0, (size_t)nT);
+            for (int64_t r = 0; r < kh[h] && r < nT; ++r)
+                Mrow[row[r].j] = 1;
+            free(row);
+        }
+    }
+    free(qb);
+    free(kb);
+}
