@@ -50,7 +50,7 @@ EXPORTED = [
     "sparse_attn_workspace_bytes", "sparse_attn_set_mask", "sparse_attn_forward",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
-    "sparse_attn_read_pair_lists",
+    "sparse_attn_read_pair_lists", "sparse_attn_select_topk",
     "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
 ]
 
@@ -99,6 +99,7 @@ _sigs = {
     "sparse_attn_unpermute": ([_vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_read_index_lists": ([_vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
     "sparse_attn_read_pair_lists": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp], ctypes.c_int),
+    "sparse_attn_select_topk": ([_vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
     "sparse_attn_mask_info": ([_vp, _P(_i64), _P(_i32), _vp], ctypes.c_int),
     "sparse_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sparse_attn_last_error": ([_vp], ctypes.c_char_p),
@@ -261,6 +262,15 @@ def sparse_attn_read_index_lists(h, row_ptr, cols, order, stream=None):
     _check(_lib.sparse_attn_read_index_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
                                              cols.numel() if cols is not None else 0,
                                              _dptr(order, "order"), _stream(stream)), h)
+
+
+def sparse_attn_select_topk(h, k_per_head, ws, bitmap, stream=None):
+    """Top-k tile bitmap from the permuted Q and K in ws (run
+    sparse_attn_permute_inputs on ws first); bitmap: device uint8
+    [heads, nT, nT]."""
+    kh = (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
+    _check(_lib.sparse_attn_select_topk(h.ptr, kh, _dptr(ws, "ws"), _nbytes(ws),
+                                        _dptr(bitmap, "bitmap"), _stream(stream)), h)
 
 
 def sparse_attn_read_pair_lists(h, row_ptr, cols, order, flag, stream=None):

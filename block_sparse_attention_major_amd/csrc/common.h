@@ -213,6 +213,14 @@ struct AttnParams {
 // accepted query-tile pairs, then the row kernel over the other query tiles.
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
 hipError_t launch_attention_rows(const Layout &L, const AttnParams &p, hipStream_t s);
+// Tile selection from the tile-major Q and K: fp32 tile means into qbar,
+// kbar ([heads][nT][D]), then per row the kh[h] best-scoring key tiles
+// (ties to the lower tile) into bitmap [heads][nT][nT].  nT <= kSelectMaxTiles.
+constexpr int kSelectMaxTiles = 8192;
+hipError_t launch_select_topk(const Layout &L, int elem_bytes, const void *q, const void *k,
+                              const int *kh, float scale, float *qbar, float *kbar, uint8_t *bitmap,
+                              hipStream_t s);
+
 // fp32 vector-ALU kernel for any supported shape; elem_bytes 4 (fp32) or 2 (bf16).
 hipError_t launch_attention_generic(const Layout &L, int elem_bytes, const AttnParams &p,
                                     hipStream_t s);

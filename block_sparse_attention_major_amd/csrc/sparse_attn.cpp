@@ -526,6 +526,44 @@ int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, con
     return sparse_attn_unpermute_output(h, ws, ws_bytes, o, stream);
 }
 
+int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, void *ws,
+                            size_t ws_bytes, uint8_t *bitmap, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_ws(h, ws, ws_bytes)))
+        return st;
+    if (!k_per_head || !bitmap)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "k_per_head and bitmap must be non-null");
+    const sa::Layout &L = h->L;
+    for (int hh = 0; hh < L.heads; ++hh)
+        if (k_per_head[hh] < 0 || k_per_head[hh] > L.nT)
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "k_per_head[%d] = %d is outside 0..%d", hh,
+                        k_per_head[hh], L.nT);
+    if (L.nT > sa::kSelectMaxTiles)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "tile selection takes at most %d tiles (%d)",
+                    sa::kSelectMaxTiles, L.nT);
+    // Scratch in the output region: tile means of Q and K (fp32), then k.
+    const WsLayout w = ws_layout(h);
+    const size_t means = sa::align256(size_t(L.heads) * L.nT * L.D * 4);
+    if (2 * means + 4 * size_t(L.heads) > w.total - w.o)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "tiles of %d slots are too small for the selection scratch",
+                    L.B);
+    char *b = static_cast<char *>(ws);
+    float *qbar = reinterpret_cast<float *>(b + w.o);
+    float *kbar = reinterpret_cast<float *>(b + w.o + means);
+    int *kh = reinterpret_cast<int *>(b + w.o + 2 * means);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(kh, k_per_head, 4 * size_t(L.heads), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = sa::launch_select_topk(L, h->elem_bytes, b + w.q, b + w.k, kh, h->scale, qbar, kbar, bitmap,
+                                   s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "tile selection");
+    return SPARSE_ATTN_OK;
+}
+
 int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32_t layout,
                         void *stream)
 {

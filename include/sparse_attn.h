@@ -213,6 +213,24 @@ int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_byte
                                  void *stream);
 
 /*
+ * Tile selection on the GPU: a top-k tile bitmap from Q and K, for
+ * sparse_attn_set_mask (SCOPE review page: the abstract names masks built
+ * from block-level proxy scores, "The reading" a per-head Top-k count;
+ * AdaSpa page, abstract: a blockified pattern).  Score of tile pair (i, j)
+ * in head h: softmax scale * qbar_i . kbar_j, with qbar, kbar the fp32 means
+ * of the tiles' real tokens; row i keeps the k_per_head[h] key tiles with
+ * the largest score, ties to the lower j.
+ * Reads the permuted Q and K in ws (call sparse_attn_permute_inputs on ws
+ * first) and uses the output region of ws as scratch.  k_per_head: host
+ * int32 [heads], each in 0..nT.  bitmap: device uint8 [heads][nT][nT], out.
+ * Errors: INVALID_ARG (null pointers, k out of range), UNSUPPORTED (more
+ * than 8192 tiles, or tiles too small for the scratch: B * elem < 8 bytes),
+ * WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, void *ws,
+                            size_t ws_bytes, uint8_t *bitmap, void *stream);
+
+/*
  * Test hooks.
  * sparse_attn_permute: src [heads][N][head_dim] raster -> dst in `layout`
  *   (SPARSE_ATTN_LAYOUT_*), empty slots zero.  dst holds heads * nT * B *

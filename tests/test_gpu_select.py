@@ -1,0 +1,137 @@
+"""GPU tile selection (mean-pooled block scores, per-head top-k) against the
+oracle's selection.
+
+The GPU scores in fp32, the oracle in fp64, so a row whose k-th and
+(k+1)-th best scores are closer than fp32 rounding may keep a different
+tile; every differing tile must be such a near-tie, and every row keeps
+exactly k tiles."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_major_amd as sa
+import oracle
+from workloads import make_workload
+
+from gpu_helpers import dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_select(h, q, k, kh):
+    L = sa.sparse_attn_layout(h)
+    heads, nT = q.shape[0], L["tiles"]
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    qd, kd = dev(q), dev(k)
+    sa.sparse_attn_permute_inputs(h, qd, kd, kd, ws)
+    bm = torch.full((heads, nT, nT), 7, dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_select_topk(h, kh, ws, bm)
+    torch.cuda.synchronize()
+    return bm.cpu().numpy()
+
+
+def _scores(grid, tile, q, k, d):
+    """fp64 block scores [heads, nT, nT] from the oracle's tile means."""
+    return np.stack([oracle.tile_means(grid, tile, q[h]) @ oracle.tile_means(grid, tile, k[h]).T
+                     for h in range(q.shape[0])]) / np.sqrt(d)
+
+
+def _check(grid, tile, q, k, kh, dtype):
+    heads, _, d = q.shape
+    h = sa.sparse_attn_create(heads, d, grid, tile, dtype)
+    got = _gpu_select(h, q, k, kh)
+    want = oracle.select_topk(grid, tile, q, k, kh)
+    assert set(np.unique(got)) <= {0, 1}
+    for hh in range(heads):
+        assert (got[hh].sum(axis=1) == kh[hh]).all()
+    diff = np.argwhere(got != want)
+    if len(diff):
+        S = _scores(grid, tile, q, k, d)
+        for hh, i, j in diff:
+            row = np.sort(S[hh, i])[::-1]
+            kk = kh[hh]
+            thr = row[kk - 1]
+            tol = 1e-5 * max(1.0, abs(thr))
+            assert abs(S[hh, i, j] - thr) <= tol, (hh, i, j, S[hh, i, j], thr)
+    return len(diff)
+
+
+def test_hunyuan_masks_match_the_oracle():
+    wl = make_workload("hunyuan", heads=6)
+    kh = wl.info["k_per_head"]
+    print(f"select hunyuan heads=6 k={kh}", flush=True)
+    n = _check(wl.grid, wl.tile, wl.q, wl.k, kh, "bf16")
+    print(f"  tiles differing from the oracle (near-ties): {n}", flush=True)
+
+
+@pytest.mark.parametrize("grid,tile,d,dtype", [
+    ((4, 8, 8), (1, 4, 4), 64, "f32"),
+    ((3, 20, 36), (1, 8, 16), 128, "bf16"),
+    ((5, 3, 3), (2, 3, 3), 64, "f32"),
+])
+def test_random_inputs_match_the_oracle(grid, tile, d, dtype):
+    heads = 3
+    N = int(np.prod(grid))
+    nT = oracle.num_tiles(grid, tile)
+    rng = np.random.default_rng([11, d, *grid])
+    q = rng.standard_normal((heads, N, d)).astype(np.float32)
+    k = rng.standard_normal((heads, N, d)).astype(np.float32)
+    if dtype == "bf16":
+        q = (q.view(np.uint32) >> 16).astype(np.uint16)
+        k = (k.view(np.uint32) >> 16).astype(np.uint16)
+    kh = [1, max(1, nT // 3), nT - 1]
+    print(f"select grid={grid} tile={tile} d={d} {dtype} k={kh}", flush=True)
+    _check(grid, tile, q, k, kh, dtype)
+
+
+def test_ties_and_ends():
+    grid, tile = (2, 12, 16), (1, 4, 8)
+    N, d = int(np.prod(grid)), 64
+    nT = oracle.num_tiles(grid, tile)
+    rng = np.random.default_rng(4)
+    q = np.zeros((4, N, d), np.float32)  # every score 0: ties everywhere
+    k = rng.standard_normal((4, N, d)).astype(np.float32)
+    kh = [0, 3, nT - 1, nT]
+    h = sa.sparse_attn_create(4, d, grid, tile, "f32")
+    got = _gpu_select(h, q, k, kh)
+    for hh, kk in enumerate(kh):
+        want = np.zeros(nT, np.uint8)
+        want[:kk] = 1
+        assert all(np.array_equal(got[hh, i], want) for i in range(nT)), hh
+
+
+def test_selected_mask_drives_the_forward():
+    """Selection -> mask compile -> attention equals the oracle's attention
+    under the oracle's selection (near-tie rows excluded)."""
+    wl = make_workload("small", heads=2)
+    nT = oracle.num_tiles(wl.grid, wl.tile)
+    kh = [nT // 4, nT // 2]
+    h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, "bf16")
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
+    sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+    bm = torch.empty((wl.heads, nT, nT), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_select_topk(h, kh, ws, bm)
+    mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_set_mask(h, mb, bitmap=bm)
+    o = torch.empty_like(q)
+    sa.sparse_attn_forward(h, q, k, v, o, ws)
+    torch.cuda.synchronize()
+    M = oracle.select_topk(wl.grid, wl.tile, wl.q, wl.k, kh)
+    assert np.array_equal(bm.cpu().numpy(), M)
+    from workloads import bf16_bits_to_f32
+    got = bf16_bits_to_f32(o.cpu().numpy().view(np.uint16)).astype(np.float64)
+    rows = np.random.default_rng(2).choice(wl.heads * wl.config.tokens, 256, replace=False)
+    want = oracle.attention_rows(wl.grid, wl.tile, wl.q, wl.k, wl.v, M, rows)
+    err = np.abs(got.reshape(-1, wl.head_dim)[rows] - want).max()
+    assert err <= 2e-2, err
+
+
+def test_select_rejects_bad_k():
+    h = sa.sparse_attn_create(2, 64, (2, 8, 8), (1, 4, 4), "f32")
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    bm = torch.empty((2, 8, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_select_topk(h, [1, 9], ws, bm)
+    assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
