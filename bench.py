@@ -199,6 +199,25 @@ def main():
         torch.cuda.synchronize()
         dense_ms = float(np.mean([a.elapsed_time(b) for a, b in dense]))
 
+    # Tile selection (the step that chooses top-k masks from Q and K; not part
+    # of the timed step): k per head from the workload when it is a top-k
+    # workload, else the workload's tile density.
+    nT = info["nT"]
+    kh = info.get("k_per_head") or [max(1, round(info["tile_density"] * nT))] * wl.heads
+    sel_bitmap = torch.empty((wl.heads, nT, nT), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+    sa.sparse_attn_select_topk(h, kh, ws, sel_bitmap)
+    sel = []
+    for _ in range(5):
+        a, b = E(), E()
+        a.record(stream)
+        sa.sparse_attn_select_topk(h, kh, ws, sel_bitmap)
+        b.record(stream)
+        sel.append((a, b))
+    torch.cuda.synchronize()
+    select_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
+    del sel_bitmap
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -248,6 +267,10 @@ def main():
         "stages_gbs": {"permute_qkv": perm_bytes / (perm_ms * 1e-3) / 1e9,
                        "unpermute_o": unperm_bytes / (unperm_ms * 1e-3) / 1e9,
                        "peak": PEAK_HBM_GBS},
+        "tile_selection": {"ms": select_ms, "k_per_head": [int(x) for x in kh],
+                           "pool_gbs": 2 * in_bytes / (select_ms * 1e-3) / 1e9,
+                           "note": "top-k over mean-pooled tile scores from the permuted Q, K; "
+                                   "not part of the timed step"},
     }
     if not args.no_cpu_baseline:
         import oracle
