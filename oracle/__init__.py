@@ -41,7 +41,8 @@ def _load():
         lib.oracle_attention_rows.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p,
-                                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
+                                              ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int]
         lib.oracle_probabilities.argtypes = [g, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
                                              ctypes.c_void_p]
@@ -127,8 +128,10 @@ def default_threads():
     return len(os.sched_getaffinity(0))
 
 
-def attention_rows(grid, tile, q, k, v, M, rows, scale=None, threads=None):
-    """fp64 outputs of the given flattened query rows (h * N + n): [len(rows), d]."""
+def attention_rows(grid, tile, q, k, v, M, rows, scale=None, threads=None, lse=False):
+    """fp64 outputs of the given flattened query rows (h * N + n): [len(rows), d].
+    With lse=True also the rows' log-sum-exp of kept scores (natural log,
+    -inf for a row that keeps nothing): returns (out, lse)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
     v = np.ascontiguousarray(v)
@@ -141,17 +144,22 @@ def attention_rows(grid, tile, q, k, v, M, rows, scale=None, threads=None):
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     out = np.empty((len(rows), d), dtype=np.float64)
+    L = np.empty(len(rows), dtype=np.float64) if lse else None
     _load().oracle_attention_rows(ctypes.byref(_grid(grid, tile)), heads, d, code, _ptr(q), _ptr(k),
                                   _ptr(v), _ptr(M), float(scale), _ptr(rows), len(rows), _ptr(out),
-                                  int(threads or default_threads()))
-    return out
+                                  _ptr(L) if lse else None, int(threads or default_threads()))
+    return (out, L) if lse else out
 
 
-def attention(grid, tile, q, k, v, M, scale=None, threads=None):
-    """fp64 outputs of every query: [heads, N, d]."""
+def attention(grid, tile, q, k, v, M, scale=None, threads=None, lse=False):
+    """fp64 outputs of every query: [heads, N, d] (with lse=True also the
+    log-sum-exp [heads, N])."""
     heads, N, d = q.shape
     rows = np.arange(heads * N, dtype=np.int64)
-    return attention_rows(grid, tile, q, k, v, M, rows, scale, threads).reshape(heads, N, d)
+    r = attention_rows(grid, tile, q, k, v, M, rows, scale, threads, lse)
+    if lse:
+        return r[0].reshape(heads, N, d), r[1].reshape(heads, N)
+    return r.reshape(heads, N, d)
 
 
 def probabilities(grid, tile, q, k, Mh, scale=None):

@@ -55,3 +55,20 @@ def attention(grid, tile, q, k, v, M, scale=None):
         P = np.divide(E, den[:, None], out=np.zeros_like(E), where=den[:, None] > 0)
         out[h] = P @ v[h]
     return out
+
+
+def lse(grid, tile, q, k, M, scale=None):
+    """Log-sum-exp of each query's kept scores: [heads, N], -inf where a row
+    keeps nothing."""
+    heads, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.full((heads, N), -np.inf)
+    for h in range(heads):
+        keep = token_mask(grid, tile, M[h])
+        S = scale * (q[h] @ k[h].T)
+        for n in range(N):
+            if keep[n].any():
+                s = S[n, keep[n]]
+                out[h, n] = s.max() + np.log(np.exp(s - s.max()).sum())
+    return out

@@ -20,6 +20,12 @@
  *    with mu the maximum score over J, all in double precision; an empty J
  *    gives O = 0.
  *
+ *  - The log-sum-exp of a query row's kept scores,
+ *        LSE[h, n] = mu + ln sum_{m in J} exp(s q_n.k_m - mu),
+ *    natural log, -infinity for an empty J.  It is the per-row statistic the
+ *    AdaSpa page (abstract) caches across denoising steps; with it the
+ *    weights of any key are exp(s q_n.k_m - LSE) without another pass.
+ *
  *  - Masks are per head and per pair of tiles (Compact Attention page,
  *    abstract: head-specific masks in one tile-aligned family; Fig. 3
  *    caption: precomputed masks are loaded into block-sparse attention
@@ -221,11 +227,13 @@ static double load_elem(const void *p, int dtype, int64_t idx)
  *   M: dense tile mask [heads][nT][nT].
  *   rows[count]: flattened query ids h * N + n.
  *   out[count][d]: fp64 outputs.
+ *   lse[count]: log-sum-exp of each row's kept scores, or NULL.
  *   scale: score scale s (the caller passes 1/sqrt(d) by default).
  */
 void oracle_attention_rows(const oracle_grid *g, int64_t heads, int64_t d, int dtype, const void *q,
                            const void *k, const void *v, const uint8_t *M, double scale,
-                           const int64_t *rows, int64_t count, double *out, int nthreads)
+                           const int64_t *rows, int64_t count, double *out, double *lse,
+                           int nthreads)
 {
     int64_t N = g->T * g->H * g->W;
     int64_t nT = oracle_num_tiles(g);
@@ -263,6 +271,8 @@ void oracle_attention_rows(const oracle_grid *g, int64_t heads, int64_t d, int d
             }
             for (int64_t e = 0; e < d; ++e)
                 acc[e] = 0.0;
+            if (lse)
+                lse[c] = -INFINITY;
             if (any) {
                 double den = 0.0;
                 for (int64_t m = 0; m < N; ++m) {
@@ -275,6 +285,8 @@ void oracle_attention_rows(const oracle_grid *g, int64_t heads, int64_t d, int d
                 }
                 for (int64_t e = 0; e < d; ++e)
                     acc[e] /= den;
+                if (lse)
+                    lse[c] = mu + log(den);
             }
             memcpy(out + c * d, acc, sizeof(double) * (size_t)d);
         }
