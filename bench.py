@@ -3,8 +3,9 @@
 One step is one pass of the whole hot path over the Wan2.1-shaped 720p
 workload (40 heads, head_dim 128, bf16, grid 21x45x80 = 75,600 tokens, tile
 1x8x16, local / axial / near-dense dual-window masks at ~26% tile density):
-mask compile -> permute Q/K/V to tile-major -> block-sparse attention ->
-unpermute O.  Inputs are synthetic and resident in HBM before timing.
+mask compile -> permute K/V to tile-major -> block-sparse attention, which
+reads Q and writes O in raster order itself.  Inputs are synthetic and
+resident in HBM before timing.
 
 Printed: one JSON line.  `value` is the effective throughput of the whole
 step, F_alg / step time, where F_alg = 4 d sum over kept tile pairs of
@@ -150,6 +151,8 @@ def main():
 
     E = lambda: torch.cuda.Event(enable_timing=True)
 
+    # sparse_attn_forward is exactly these two stages; they are called one by
+    # one so the attention launches can be timed on their own.
     def step(ev=None):
         if ev is None:
             set_mask()
@@ -158,17 +161,15 @@ def main():
         ev[0].record(stream)
         set_mask()
         ev[1].record(stream)
-        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        sa.sparse_attn_permute_kv(h, k, v, ws)
         ev[2].record(stream)
-        sa.sparse_attn_attend(h, ws)
+        sa.sparse_attn_attend_raster(h, q, o, ws)
         ev[3].record(stream)
-        sa.sparse_attn_unpermute_output(h, ws, o)
-        ev[4].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[E() for _ in range(5)] for _ in range(args.steps)]
+    events = [[E() for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -176,9 +177,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events])  # ms
-    mask_ms, perm_ms, attn_ms, unperm_ms = st.mean(axis=0)
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events])  # ms
+    mask_ms, perm_ms, attn_ms = st.mean(axis=0)
     attn_min = st[:, 2].min()
+
+    # The same attention launches also writing the per-query log-sum-exp.
+    lse = torch.empty((wl.heads, cfg.tokens), dtype=torch.float32, device="cuda")
+    sa.sparse_attn_attend_raster(h, q, o, ws, lse=lse)
+    lse_ev = []
+    for _ in range(5):
+        a, b = E(), E()
+        a.record(stream)
+        sa.sparse_attn_attend_raster(h, q, o, ws, lse=lse)
+        b.record(stream)
+        lse_ev.append((a, b))
+    torch.cuda.synchronize()
+    attn_lse_ms = float(np.mean([a.elapsed_time(b) for a, b in lse_ev]))
+    del lse
     nnz, overflow = sa.sparse_attn_mask_info(h)
     assert nnz == info["nnz"] and not overflow, (nnz, info["nnz"], overflow)
 
@@ -186,14 +201,14 @@ def main():
     dense_ms = None
     if not args.no_dense:
         sa.sparse_attn_set_mask(h, dense_buf, bitmap=ones)
-        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        sa.sparse_attn_permute_kv(h, k, v, ws)
         for _ in range(2):
-            sa.sparse_attn_attend(h, ws)
+            sa.sparse_attn_attend_raster(h, q, o, ws)
         dense = []
         for _ in range(max(3, args.steps // 4)):
             a, b = E(), E()
             a.record(stream)
-            sa.sparse_attn_attend(h, ws)
+            sa.sparse_attn_attend_raster(h, q, o, ws)
             b.record(stream)
             dense.append((a, b))
         torch.cuda.synchronize()
@@ -231,8 +246,7 @@ def main():
     attn_tflops = F / (attn_ms * 1e-3) / 1e12
     in_bytes = heads * N * d * elem
     slot_bytes = heads * info["nT"] * info["tile_volume"] * d * elem
-    perm_bytes = 3 * (in_bytes + slot_bytes)
-    unperm_bytes = 2 * in_bytes  # real rows read, raster rows written
+    perm_bytes = 2 * (in_bytes + slot_bytes)  # K and V: raster read, tile-major written
     traffic = traffic_per_launch(args.workload)
     result = {
         "metric": METRIC,
@@ -251,7 +265,8 @@ def main():
                    "grid": list(cfg.grid), "tile": list(cfg.tile), "tokens": N,
                    "tile_density": round(info["tile_density"], 5),
                    "token_density": round(info["token_density"], 5),
-                   "step": "mask compile + permute + block-sparse attention + unpermute"},
+                   "step": "mask compile + permute K, V + block-sparse attention (Q read and O "
+                           "written in raster order by the attention kernels)"},
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F},
@@ -261,12 +276,10 @@ def main():
                       "dense_ms": dense_ms,
                       "dense_speedup": dense_ms / attn_ms if dense_ms else None,
                       "ideal_speedup": info["flops_dense"] / F,
-                      "dense_tflops": info["flops_dense"] / (dense_ms * 1e-3) / 1e12 if dense_ms else None},
-        "stages_ms": {"mask_compile": mask_ms, "permute_qkv": perm_ms, "attention": attn_ms,
-                      "unpermute_o": unperm_ms},
-        "stages_gbs": {"permute_qkv": perm_bytes / (perm_ms * 1e-3) / 1e9,
-                       "unpermute_o": unperm_bytes / (unperm_ms * 1e-3) / 1e9,
-                       "peak": PEAK_HBM_GBS},
+                      "dense_tflops": info["flops_dense"] / (dense_ms * 1e-3) / 1e12 if dense_ms else None,
+                      "with_lse_ms": attn_lse_ms},
+        "stages_ms": {"mask_compile": mask_ms, "permute_kv": perm_ms, "attention": attn_ms},
+        "stages_gbs": {"permute_kv": perm_bytes / (perm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS},
         "tile_selection": {"ms": select_ms, "k_per_head": [int(x) for x in kh],
                            "pool_gbs": 2 * in_bytes / (select_ms * 1e-3) / 1e9,
                            "note": "top-k over mean-pooled tile scores from the permuted Q, K; "

@@ -48,6 +48,7 @@ SPARSE_ATTN_MAX_GROUPS = 8
 EXPORTED = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_layout", "sparse_attn_mask_bytes",
     "sparse_attn_workspace_bytes", "sparse_attn_set_mask", "sparse_attn_forward",
+    "sparse_attn_forward_lse", "sparse_attn_permute_kv", "sparse_attn_attend_raster",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
     "sparse_attn_read_pair_lists", "sparse_attn_select_topk",
@@ -92,6 +93,9 @@ _sigs = {
     "sparse_attn_workspace_bytes": ([_vp, _P(_sz)], ctypes.c_int),
     "sparse_attn_set_mask": ([_vp, _P(sparse_attn_mask), _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_forward_lse": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_permute_kv": ([_vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_attend_raster": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_permute_inputs": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_attend": ([_vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_unpermute_output": ([_vp, _vp, _sz, _vp, _vp], ctypes.c_int),
@@ -233,6 +237,23 @@ def sparse_attn_set_mask(h, mask_buf, bitmap=None, groups=None, groups_per_head=
 def sparse_attn_forward(h, q, k, v, o, ws, stream=None):
     _check(_lib.sparse_attn_forward(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"), _dptr(o, "o"),
                                     _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_forward_lse(h, q, k, v, o, lse, ws, stream=None):
+    """Forward that also writes lse (device fp32 [heads, N], or None)."""
+    _check(_lib.sparse_attn_forward_lse(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"),
+                                        _dptr(o, "o"), _dptr(lse, "lse"), _dptr(ws, "ws"),
+                                        _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_permute_kv(h, k, v, ws, stream=None):
+    _check(_lib.sparse_attn_permute_kv(h.ptr, _dptr(k, "k"), _dptr(v, "v"), _dptr(ws, "ws"),
+                                       _nbytes(ws), _stream(stream)), h)
+
+
+def sparse_attn_attend_raster(h, q, o, ws, lse=None, stream=None):
+    _check(_lib.sparse_attn_attend_raster(h.ptr, _dptr(q, "q"), _dptr(o, "o"), _dptr(lse, "lse"),
+                                          _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
 
 
 def sparse_attn_permute_inputs(h, q, k, v, ws, stream=None):

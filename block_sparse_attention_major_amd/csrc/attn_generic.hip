@@ -46,8 +46,11 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
     const bool active = slot < L.B && slot < ci;
     const float sl2 = P.scale_log2;
 
+    // Row of this slot's query in q and o: the raster token (raster I/O) or
+    // the tile-major slot.
+    const int tok = (active && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const long long qrow = P.raster ? (long long)h * L.N + tok : (long long)h * L.Npad + (long long)i * L.B + slot;
     float q[DH], o[DH];
-    const long long qrow = (long long)h * L.Npad + (long long)i * L.B + slot;
 #pragma unroll
     for (int e = 0; e < DH; ++e) {
         q[e] = active ? to_f32(Qp[qrow * D + part * DH + e]) * sl2 : 0.f;
@@ -109,6 +112,9 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
     }
     if (active) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
+        // m is in log2 units (q carries scale * log2 e) and l sums exp2(s - m).
+        if (P.lse && part == 0)
+            P.lse[(long long)h * L.N + tok] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 #pragma unroll
         for (int e = 0; e < DH; ++e)
             store_as(&Op[qrow * D + part * DH + e], o[e] * inv);

@@ -451,11 +451,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     const bool wave_active = sub * 32 < ci;
     const int my_bit = 1 << side;
 
+    // This lane's query: slot sub * 32 + l32 of tile i, a real token when
+    // the slot is below c_i.  Its row in q and o is the raster token
+    // (raster I/O, real slots only) or the tile-major slot.
+    const int slot = sub * 32 + l32;
+    const bool q_real = slot < ci;
+    const int tok = (q_real && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const long long qrow = P.raster ? (long long)h * L.N + tok
+                                    : (long long)h * L.Npad + (long long)max(i, 0) * kTile + slot;
+    const bool q_io = wave_active && (q_real || !P.raster);
+    // Where this query's log-sum-exp goes (one lane per query), or null.
+    float *lse_at = (P.lse && q_real && hi == 0) ? P.lse + (long long)h * L.N + tok : nullptr;
+
     // Q operand (B of S^T = K Q^T): lane holds query l32, features
     // 16 ks + 8 hi .. +7 for every k-step.
-    const long long qrow = (long long)h * L.Npad + (long long)max(i, 0) * kTile + sub * 32 + l32;
     bf16x8 qf[KS];
-    if (wave_active) {
+    if (q_io) {
         const bf16x8 *qp = (const bf16x8 *)(Qp + qrow * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -650,9 +661,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         lds_barrier();  // pairs with B's extra barrier: both groups pass the same count
     wait_vmcnt<0>();  // no copy may land after the workgroup ends
 
-    if (wave_active) {
-        const float lt = half_sum(st.l);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // half_sum exchanges lanes l and l ^ 32, so it runs with the whole wave.
+    const float lt = wave_active ? half_sum(st.l) : 0.f;
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // st.m is in log2 units and st.l sums exp2(score * log2 e - st.m).
+    if (lse_at)
+        *lse_at = lt > 0.f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
+    if (q_io) {
         uint16_t *orow = Op + qrow * D;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {

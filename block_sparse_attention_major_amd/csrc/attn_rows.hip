@@ -300,15 +300,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
     const int ci = tile_tokens(L, P, i);
     const bool wave_active = wave * 32 < ci;
 
+    // This lane's query: slot wave * 32 + l32 of tile i, a real token when
+    // the slot is below c_i.  Its row in q and o is the raster token
+    // (raster I/O, real slots only) or the tile-major slot.
+    const int slot = wave * 32 + l32;
+    const bool q_real = slot < ci;
+    const int tok = (q_real && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const long long qrow = P.raster ? (long long)h * L.N + tok
+                                    : (long long)h * L.Npad + (long long)i * kTile + slot;
+    const bool q_io = q_real || !P.raster;
+    // Where this query's log-sum-exp goes (one lane per query), or null.
+    float *lse_at = (P.lse && q_real && hi == 0) ? P.lse + (long long)h * L.N + tok : nullptr;
+
     // Q operand (B of S^T = K Q^T): lane holds query l32, features
     // 16 ks + 8 hi .. +7 for every k-step.
-    const long long qrow = (long long)h * L.Npad + (long long)i * kTile + wave * 32 + l32;
     bf16x8 qf[KS];
-    {
+    if (q_io) {
         const bf16x8 *qp = (const bf16x8 *)(Qp + qrow * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = qp[2 * ks + hi];
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                qf[ks][u] = (__bf16)0.0f;
     }
     RowState<D> st;
 #pragma unroll
@@ -392,6 +409,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
     if (wave_active) {
         const float lt = half_sum(st.l);
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        // st.m is in log2 units and st.l sums exp2(score * log2 e - st.m).
+        if (lse_at)
+            *lse_at = lt > 0.f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
+        if (!q_io)
+            return;
         uint16_t *orow = Op + qrow * D;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {

@@ -59,6 +59,15 @@ __host__ __device__ inline int tile_real_count(const Layout &L, int tau)
     return r.et * r.ey * r.ex;
 }
 
+// Raster token id of real slot s (0 <= s < c_tau) of the tile with box bx.
+__host__ __device__ inline int slot_token(const Layout &L, const TileBox &bx, int s)
+{
+    const int plane = bx.ey * bx.ex;
+    const int lt = s / plane, rem = s - lt * plane;
+    const int ly = rem / bx.ex, lx = rem - ly * bx.ex;
+    return ((bx.a * L.tt + lt) * L.H + bx.b * L.th + ly) * L.W + bx.e * L.tw + lx;
+}
+
 // The query tiles of pair pr (raster over the pair grid); t2 = -1 when the
 // first tile is alone.
 struct TilePair {
@@ -139,6 +148,8 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f)
     return (__umulhi(n, f.m) + n) >> f.s;
 }
 
+constexpr float kLn2 = 0.69314718055994531f;
+
 // Round a byte count up to a 256-byte boundary.
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -196,10 +207,13 @@ struct ListSet {
 };
 
 struct AttnParams {
-    const void *q;      // tile-major rows
+    const void *q;      // tile-major rows, or raster rows when raster = 1
     const void *k;      // tile-major rows
     const void *v;      // tile-major rows (generic) or tile columns (MFMA)
-    void *o;            // tile-major rows
+    void *o;            // tile-major rows, or raster rows when raster = 1
+    int raster;         // 1: q is read from and o written to [heads][N][D] in raster
+                        //    order (real slots only); 0: both tile-major
+    float *lse;         // null, or [heads][N] raster: ln sum over kept keys of exp(score)
     ListSet rows;       // per query tile
     ListSet pairs;      // per query-tile pair (matrix-core kernels only)
     const int *pair_flag;  // [heads nP] (matrix-core kernels only)

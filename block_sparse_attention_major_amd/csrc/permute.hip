@@ -72,10 +72,7 @@ __global__ __launch_bounds__(kThreads) void permute_tile_columns_kernel(
         const int slot = u / WPR, w = u - slot * WPR;
         uint32_t val = 0;
         if (slot < c) {
-            const int ex = bx.ex, ey = bx.ey;
-            const int lt = slot / (ey * ex), ly = (slot / ex) % ey, lx = slot % ex;
-            const long long n = ((long long)(bx.a * L.tt + lt) * L.H + (bx.b * L.th + ly)) * L.W +
-                                (bx.e * L.tw + lx);
+            const long long n = slot_token(L, bx, slot);
             val = reinterpret_cast<const uint32_t *>(src + ((long long)h * L.N + n) * D)[w];
         }
         tileT[slot * LD + 2 * w] = (uint16_t)(val & 0xFFFF);

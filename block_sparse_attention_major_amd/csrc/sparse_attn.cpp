@@ -160,6 +160,8 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     p.k = b + w.k;
     p.v = b + w.v;
     p.o = b + w.o;
+    p.raster = 0;
+    p.lse = nullptr;
     p.rows = sa::ListSet{h->mb.row_ptr, h->mb.cols, h->mb.order, h->mb.cap};
     p.pairs = sa::ListSet{h->pb.row_ptr, h->pb.cols, h->pb.order, h->pb.cap};
     p.pair_flag = h->pb.flag;
@@ -171,6 +173,16 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     p.div_row = sa::make_fastdiv(uint32_t(h->L.nx));
     return p;
 }
+
+hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p, hipStream_t s)
+{
+    if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
+        return sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
+    hipError_t e = sa::launch_attention_mfma(h->L, p, s);
+    return e == hipSuccess ? sa::launch_attention_rows(h->L, p, s) : e;
+}
+
+size_t lse_bytes(const sparse_attn_handle *h) { return size_t(h->L.heads) * h->L.N * sizeof(float); }
 
 }  // namespace
 
@@ -471,16 +483,7 @@ int sparse_attn_attend(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *s
         return st;
     if (!h->has_mask)
         return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before attention");
-    const sa::AttnParams p = attn_params(h, ws);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16) {
-        e = sa::launch_attention_mfma(h->L, p, s);
-        if (e == hipSuccess)
-            e = sa::launch_attention_rows(h->L, p, s);
-    } else {
-        e = sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
-    }
+    const hipError_t e = launch_attention(h, attn_params(h, ws), static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return hip_fail(h, e, "attention launch");
     return SPARSE_ATTN_OK;
@@ -504,8 +507,63 @@ int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_byte
     return SPARSE_ATTN_OK;
 }
 
-int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
-                        void *ws, size_t ws_bytes, void *stream)
+int sparse_attn_permute_kv(sparse_attn_handle *h, const void *k, const void *v, void *ws,
+                           size_t ws_bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, k, "k")) || (st = check_io(h, v, "v")) || (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    const size_t n = io_bytes(h);
+    const WsLayout w = ws_layout(h);
+    for (const void *p : {k, v})
+        if (overlaps(p, n, ws, w.total))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "inputs must not overlap the workspace");
+    char *b = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_permute_rows(h->L, h->elem_bytes, k, b + w.k, s);
+    if (e == hipSuccess)
+        e = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16
+                ? sa::launch_permute_tile_columns(h->L, v, b + w.v, s)
+                : sa::launch_permute_rows(h->L, h->elem_bytes, v, b + w.v, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "permute launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_attend_raster(sparse_attn_handle *h, const void *q, void *o, float *lse, void *ws,
+                              size_t ws_bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, q, "q")) || (st = check_io(h, o, "o")) || (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    if (lse && !aligned16(lse))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lse is not 16-byte aligned");
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before attention");
+    const size_t n = io_bytes(h);
+    const WsLayout w = ws_layout(h);
+    if (overlaps(o, n, q, n) || overlaps(o, n, ws, w.total) || overlaps(q, n, ws, w.total))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "q, o and the workspace must not overlap");
+    if (lse && (overlaps(lse, lse_bytes(h), q, n) || overlaps(lse, lse_bytes(h), o, n) ||
+                overlaps(lse, lse_bytes(h), ws, w.total)))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lse must not overlap q, o or the workspace");
+    sa::AttnParams p = attn_params(h, ws);
+    p.q = q;
+    p.o = o;
+    p.raster = 1;
+    p.lse = lse;
+    const hipError_t e = launch_attention(h, p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(h, e, "attention launch");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_forward_lse(sparse_attn_handle *h, const void *q, const void *k, const void *v,
+                            void *o, float *lse, void *ws, size_t ws_bytes, void *stream)
 {
     if (check_handle(h))
         return SPARSE_ATTN_INVALID_ARG;
@@ -513,17 +571,33 @@ int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, con
     if ((st = check_io(h, q, "q")) || (st = check_io(h, k, "k")) || (st = check_io(h, v, "v")) ||
         (st = check_io(h, o, "o")) || (st = check_ws(h, ws, ws_bytes)))
         return st;
+    if (lse && !aligned16(lse))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lse is not 16-byte aligned");
     if (!h->has_mask)
         return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before forward");
     const size_t n = io_bytes(h);
     for (const void *p : {q, k, v})
-        if (overlaps(o, n, p, n))
-            return fail(h, SPARSE_ATTN_INVALID_ARG, "o must not overlap q, k or v");
-    if ((st = sparse_attn_permute_inputs(h, q, k, v, ws, ws_bytes, stream)))
+        if (overlaps(o, n, p, n) || (lse && overlaps(lse, lse_bytes(h), p, n)))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "o and lse must not overlap q, k or v");
+    if (lse && overlaps(lse, lse_bytes(h), o, n))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lse must not overlap o");
+    const size_t wt = ws_layout(h).total;
+    for (const void *p : {q, k, v, static_cast<const void *>(o)})
+        if (overlaps(p, n, ws, wt))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "q, k, v and o must not overlap the workspace");
+    if (lse && overlaps(lse, lse_bytes(h), ws, wt))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lse must not overlap the workspace");
+    // Every check of the two stages has passed here, so nothing is enqueued
+    // unless both launch.
+    if ((st = sparse_attn_permute_kv(h, k, v, ws, ws_bytes, stream)))
         return st;
-    if ((st = sparse_attn_attend(h, ws, ws_bytes, stream)))
-        return st;
-    return sparse_attn_unpermute_output(h, ws, ws_bytes, o, stream);
+    return sparse_attn_attend_raster(h, q, o, lse, ws, ws_bytes, stream);
+}
+
+int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
+                        void *ws, size_t ws_bytes, void *stream)
+{
+    return sparse_attn_forward_lse(h, q, k, v, o, nullptr, ws, ws_bytes, stream);
 }
 
 int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, void *ws,

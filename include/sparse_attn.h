@@ -24,7 +24,8 @@
  * Calling pattern (mirrors the pages' offline/online split):
  *     sparse_attn_create        once per shape (host only)
  *     sparse_attn_set_mask      once per mask; compiles it on the GPU
- *     sparse_attn_forward       many times; permute -> attend -> unpermute
+ *     sparse_attn_forward       many times; permute K, V -> attend (Q read and O
+ *                               written in place, raster order)
  *     sparse_attn_destroy
  *
  * Conventions shared by every entry point:
@@ -196,16 +197,45 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
 /*
  * Block-sparse attention forward.  q, k, v, o: device [heads][T*H*W][head_dim]
  * in raster token order, element type cfg.dtype; o must not overlap q, k, v
- * or ws.  ws: device workspace of at least sparse_attn_workspace_bytes.
- * Enqueues permute (Q, K, V to tile-major) -> attention over the kept tile
- * pairs -> unpermute (O back to raster order).
+ * or ws, and none of them may overlap ws.  ws: device workspace of at least
+ * sparse_attn_workspace_bytes.  Enqueues the permute of K and V to the
+ * tile-major layout, then attention over the kept tile pairs, which reads
+ * each query row of q and writes its row of o directly (the permute of Q and
+ * the unpermute of O are fused into the attention kernels).  Only the K and
+ * V regions of ws are used.  The result is bit-identical to the three-stage
+ * path below.
  * Errors: INVALID_ARG, NO_MASK, WORKSPACE_TOO_SMALL, HIP_ERROR.
  */
 int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
                         void *ws, size_t ws_bytes, void *stream);
 
-/* The three stages of sparse_attn_forward, callable one by one (same
- * arguments and errors); forward is exactly these in order. */
+/*
+ * sparse_attn_forward that also returns, per query, the log-sum-exp of its
+ * kept scores: lse[h][n] = ln sum over kept keys m of exp(s q_n . k_m)
+ * (natural log; -infinity for a query whose tile keeps nothing, whose o row
+ * is 0).  This is the per-row softmax statistic that the AdaSpa page
+ * (abstract) caches across denoising steps: with it, the weight of any key
+ * is exp(s q_n . k_m - lse) without another pass.  lse: device fp32
+ * [heads][T*H*W] in raster order, 16-byte aligned, overlapping none of q,
+ * k, v, o, ws; NULL = none (then this is sparse_attn_forward).  It is
+ * computed from the same running max and row sum that normalize o.
+ * Errors: as sparse_attn_forward.
+ */
+int sparse_attn_forward_lse(sparse_attn_handle *h, const void *q, const void *k, const void *v,
+                            void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/* The two stages of sparse_attn_forward(_lse), callable one by one (same
+ * arguments and errors): permute K and V into ws, then attention reading q
+ * and writing o (and lse, may be NULL) in raster order. */
+int sparse_attn_permute_kv(sparse_attn_handle *h, const void *k, const void *v, void *ws,
+                           size_t ws_bytes, void *stream);
+int sparse_attn_attend_raster(sparse_attn_handle *h, const void *q, void *o, float *lse, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/* The three-stage path, for callers that want the tile-major tensors (the
+ * tile selection reads the permuted Q and K): permute Q, K, V into ws;
+ * attention from and to ws; unpermute O out of ws.  In order, they give
+ * the same o as sparse_attn_forward, bit for bit. */
 int sparse_attn_permute_inputs(sparse_attn_handle *h, const void *q, const void *k, const void *v,
                                void *ws, size_t ws_bytes, void *stream);
 int sparse_attn_attend(sparse_attn_handle *h, void *ws, size_t ws_bytes, void *stream);

@@ -49,3 +49,34 @@ def assert_close(got, want, dtype, what=""):
         assert e["max_abs"] <= BF16_TOL, e
         assert e["rel_rms"] <= BF16_REL_RMS, e
     return e
+
+
+def lse_bound(q_rows, k_max_norm, n_kept, d, scale, dtype, lse_ref):
+    """Per-row bound on |LSE_gpu - LSE_exact| from the kernels' arithmetic.
+
+    - Scores are fp32 dot products of d terms: |error| <= d 2^-24 s |q| |k|
+      (Cauchy-Schwarz), and LSE moves by at most the largest score error.
+    - The row sum adds n_kept positive fp32 terms: relative error
+      <= n_kept 2^-24, i.e. that much in LSE.
+    - On the bf16 path each probability is rounded to bf16 before it is
+      summed (relative 2^-9), the same rounded values that weight V.
+    - exp2/log2 and the final scaling: a few ulp of max(1, |LSE|)."""
+    u = 2.0 ** -24
+    qn = np.linalg.norm(q_rows, axis=-1)
+    t = d * u * scale * qn * k_max_norm + n_kept * u + 8 * u * np.maximum(1.0, np.abs(lse_ref))
+    if dtype == "bf16":
+        t = t + 2.0 ** -9
+    return t + 1e-7
+
+
+def assert_lse_close(got, want, bound, what=""):
+    """-inf exactly where the oracle has -inf; elsewhere within the bound."""
+    inf_w = np.isneginf(want)
+    assert np.array_equal(np.isneginf(got), inf_w), what
+    fin = ~inf_w
+    assert np.all(np.isfinite(got[fin])), what
+    err = np.abs(got[fin] - want[fin])
+    worst = float((err / bound[fin]).max()) if fin.any() else 0.0
+    print(f"{what} lse max_abs={float(err.max()) if fin.any() else 0.0:.3e} "
+          f"max err/bound={worst:.3f}", flush=True)
+    assert worst <= 1.0, what

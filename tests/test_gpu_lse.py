@@ -1,0 +1,195 @@
+"""GPU parity of the log-sum-exp output and of the fused forward.
+
+sparse_attn_forward lets the attention kernels read Q and write O in raster
+order (the Q permute and the O unpermute are fused into them); its O must
+equal the three-stage path's bit for bit, on every kernel.  The LSE of each
+query (natural log of the sum of exp(score) over its kept keys, -inf for a
+query whose tile keeps nothing) is compared with the oracle's within a
+per-row bound derived from the arithmetic (gpu_helpers.lse_bound)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_major_amd as sa
+import oracle
+from workloads import f32_to_bf16_bits, make_workload
+
+from gpu_helpers import as_f64, assert_close, assert_lse_close, dev, host, lse_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, seed, dtype):
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    return x if dtype == "f32" else f32_to_bf16_bits(x)
+
+
+class Inputs:
+    def __init__(self, grid, tile, q, k, v, dtype, M, scale=0.0):
+        self.grid, self.tile, self.q, self.k, self.v = grid, tile, q, k, v
+        self.dtype, self.M, self.scale = dtype, M, scale
+        self.heads, self.N, self.d = q.shape
+
+    def oracle_scale(self):
+        return self.scale if self.scale > 0 else 1.0 / np.sqrt(self.d)
+
+
+def _random_inputs(grid, tile, d, dtype, heads=3, p=0.4, seed=0):
+    N = int(np.prod(grid))
+    nT = oracle.num_tiles(grid, tile)
+    q, k, v = (_rand((heads, N, d), seed + s, dtype) for s in (1, 2, 3))
+    M = (np.random.default_rng(seed + 4).random((heads, nT, nT)) < p).astype(np.uint8)
+    M[0, nT // 2, :] = 0  # a query tile that keeps nothing
+    return Inputs(grid, tile, q, k, v, dtype, M)
+
+
+def _gpu(c, mode):
+    """o (numpy, input dtype) and lse (numpy fp32 or None) of one path."""
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale)
+    mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.M))
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    o = torch.full_like(q, 0x7FC0 if c.dtype == "bf16" else 0)
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    lse = None
+    if mode == "forward":
+        sa.sparse_attn_forward(h, q, k, v, o, ws)
+    elif mode == "forward_lse":
+        lse = torch.full((c.heads, c.N), 12345.0, dtype=torch.float32, device="cuda")
+        sa.sparse_attn_forward_lse(h, q, k, v, o, lse, ws)
+    elif mode == "two_stage":
+        lse = torch.full((c.heads, c.N), 12345.0, dtype=torch.float32, device="cuda")
+        sa.sparse_attn_permute_kv(h, k, v, ws)
+        sa.sparse_attn_attend_raster(h, q, o, ws, lse=lse)
+    else:  # the three-stage path through the tile-major workspace
+        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        sa.sparse_attn_attend(h, ws)
+        sa.sparse_attn_unpermute_output(h, ws, o)
+    torch.cuda.synchronize()
+    return host(o, c.q), (lse.cpu().numpy() if lse is not None else None)
+
+
+def _kept_keys(c):
+    """Real kept keys of every query: [heads, N]."""
+    counts = oracle.tile_counts(c.grid, c.tile)
+    _, pos = oracle.perm(c.grid, c.tile)
+    B = int(np.prod(c.tile))
+    tile_of = pos // B
+    per_tile = c.M.astype(np.int64) @ counts  # [heads, nT]
+    return per_tile[:, tile_of]
+
+
+def _check_lse(c, got_lse, what, rows=None):
+    """Compare the GPU LSE with the oracle's (all rows, or flattened rows)."""
+    kmax = np.array([np.linalg.norm(as_f64(c.k[h]), axis=-1).max() for h in range(c.heads)])
+    kept = _kept_keys(c).reshape(-1)
+    if rows is None:
+        rows = np.arange(c.heads * c.N)
+    _, want = oracle.attention_rows(c.grid, c.tile, c.q, c.k, c.v, c.M, rows,
+                                    scale=c.oracle_scale(), lse=True)
+    hh = rows // c.N
+    q_rows = as_f64(c.q.reshape(-1, c.d)[rows])
+    bound = lse_bound(q_rows, kmax[hh], kept[rows], c.d, c.oracle_scale(), c.dtype, want)
+    assert_lse_close(got_lse.reshape(-1)[rows].astype(np.float64), want, bound, what)
+
+
+SHAPES = [
+    ((3, 20, 36), (1, 8, 16), 128, "bf16"),   # pair + row kernels, clipped tiles
+    ((3, 20, 36), (1, 8, 16), 64, "bf16"),    # head_dim 64 on the matrix cores
+    ((1, 5, 7), (1, 8, 16), 128, "bf16"),     # one tile, larger than the grid
+    ((2, 17, 33), (2, 4, 16), 128, "bf16"),   # clipped along t, y and x
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # B = 32: vector-ALU kernel
+    ((3, 10, 12), (1, 4, 8), 128, "f32"),
+    ((2, 5, 7), (2, 2, 3), 64, "f32"),
+]
+
+
+@pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
+def test_fused_forward_equals_three_stages(grid, tile, d, dtype):
+    c = _random_inputs(grid, tile, d, dtype)
+    print(f"fused vs stages grid={grid} tile={tile} d={d} {dtype}", flush=True)
+    fused, _ = _gpu(c, "forward")
+    staged, _ = _gpu(c, "stages")
+    with_lse, _ = _gpu(c, "forward_lse")
+    two, _ = _gpu(c, "two_stage")
+    assert np.array_equal(fused, staged)
+    assert np.array_equal(fused, with_lse)
+    assert np.array_equal(fused, two)
+
+
+@pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
+def test_lse_matches_the_oracle(grid, tile, d, dtype):
+    c = _random_inputs(grid, tile, d, dtype)
+    print(f"lse grid={grid} tile={tile} d={d} {dtype}", flush=True)
+    o, lse = _gpu(c, "forward_lse")
+    _check_lse(c, lse, "ragged")
+    want = oracle.attention(c.grid, c.tile, c.q, c.k, c.v, c.M, scale=c.oracle_scale())
+    assert_close(as_f64(o), want, dtype, "ragged o")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_lse_on_workloads(name):
+    wl = make_workload(name, heads=4 if name == "small" else None)
+    M = oracle.mask_of(wl)
+    c = Inputs(wl.grid, wl.tile, wl.q, wl.k, wl.v, wl.dtype, M)
+    print(f"lse {name} heads={c.heads}", flush=True)
+    _, lse = _gpu(c, "forward_lse")
+    _check_lse(c, lse, name)
+
+
+def test_lse_explicit_scale():
+    c = _random_inputs((2, 16, 32), (1, 8, 16), 128, "bf16")
+    c.scale = 0.05
+    _, lse = _gpu(c, "forward_lse")
+    _check_lse(c, lse, "scale 0.05")
+
+
+def test_lse_all_rows_empty():
+    c = _random_inputs((2, 16, 32), (1, 8, 16), 128, "bf16", p=0.0)
+    o, lse = _gpu(c, "forward_lse")
+    assert np.all(np.isneginf(lse))
+    assert np.all(as_f64(o) == 0.0)
+
+
+def test_lse_full_size_wan_sampled():
+    """The Wan-shaped workload at full size, in the bench's launch
+    configuration; LSE of sampled queries (every head: the first, last and
+    a clipped query tile, plus random tokens) against the oracle."""
+    wl = make_workload("wan")
+    M = oracle.mask_of(wl)
+    c = Inputs(wl.grid, wl.tile, wl.q, wl.k, wl.v, wl.dtype, M)
+    print(f"lse wan full heads={c.heads}", flush=True)
+    _, lse = _gpu(c, "forward_lse")
+    rng = np.random.default_rng(3)
+    B = int(np.prod(wl.tile))
+    perm, _ = oracle.perm(wl.grid, wl.tile)
+    counts = oracle.tile_counts(wl.grid, wl.tile)
+    clipped = int(np.nonzero(counts < B)[0][0])
+    rows = []
+    for h in range(c.heads):
+        for t in (0, clipped, len(counts) - 1):
+            toks = perm[t * B:t * B + counts[t]]
+            rows += (h * c.N + rng.choice(toks, size=4, replace=False)).tolist()
+        rows += (h * c.N + rng.choice(c.N, size=8, replace=False)).tolist()
+    _check_lse(c, lse, "wan sampled", rows=np.array(rows, dtype=np.int64))
+    assert np.all(np.isfinite(lse[:, ::991]))
+
+
+def test_lse_argument_checks():
+    c = _random_inputs((2, 16, 32), (1, 8, 16), 128, "bf16")
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype)
+    mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.M))
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    o = torch.empty_like(q)
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    buf = torch.empty(c.heads * c.N + 4, dtype=torch.float32, device="cuda")
+    for bad in (buf[1:1 + c.heads * c.N], q):  # misaligned; overlapping q
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_forward_lse(h, q, k, v, o, bad, ws)
+        assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_attend_raster(h, q, o, ws, lse=buf[1:1 + c.heads * c.N])
+    assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    torch.cuda.synchronize()
