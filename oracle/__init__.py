@@ -51,6 +51,11 @@ def _load():
         lib.oracle_select_topk.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
+        lib.oracle_hilbert_index.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64]
+        lib.oracle_hilbert_index.restype = ctypes.c_uint64
+        lib.oracle_hilbert_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_void_p]
         _lib = lib
     return _lib
 
@@ -91,6 +96,22 @@ def perm(grid, tile):
     q = np.empty(N, dtype=np.int64)
     _load().oracle_perm(ctypes.byref(_grid(grid, tile)), _ptr(p), _ptr(q))
     return p, q
+
+
+def hilbert_index(k, t, y, x):
+    """Index of cell (t, y, x) on the 3D Hilbert curve over a 2^k cube."""
+    return int(_load().oracle_hilbert_index(int(k), int(t), int(y), int(x)))
+
+
+def hilbert_order(grid):
+    """seq[N]: raster token of each Hilbert rank (cube points outside the
+    grid skipped).  Runs of B consecutive ranks are the blocks of the
+    Hilbert layout, i.e. the tiles of a (1, 1, N) grid with tile (1, 1, B)
+    over the tokens taken in this order."""
+    T, H, W = (int(v) for v in grid)
+    seq = np.empty(T * H * W, dtype=np.int64)
+    _load().oracle_hilbert_order(T, H, W, _ptr(seq))
+    return seq
 
 
 def mask_from_windows(grid, tile, groups, groups_per_head):

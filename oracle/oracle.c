@@ -125,6 +125,92 @@ void oracle_perm(const oracle_grid *g, int64_t *perm, int64_t *pos)
 }
 
 /*
+ * Hilbert-curve token order (DFSAttn page, abstract: tokens are reordered
+ * along a Hilbert curve so that runs of consecutive tokens are compact in
+ * space, which keeps block-sparse execution efficient at a finer grain).
+ * The page gives no construction; the one used here is the 3D Hilbert curve
+ * of J. Skilling, "Programming the Hilbert curve", AIP Conf. Proc. 707
+ * (2004), over the smallest cube of side 2^k that holds the grid, with axes
+ * (t, y, x): the coordinates are turned into Skilling's transposed index,
+ * whose bits are then read level by level from the top, t's bit first.
+ * Tokens are ranked by that index (cube points outside the grid are
+ * skipped); runs of B consecutive ranks then take the place of tiles, so
+ * the layout is the tile layout of a 1 x 1 x N grid in rank order.
+ */
+static int cube_order(int64_t T, int64_t H, int64_t W)
+{
+    int64_t m = T > H ? T : H;
+    if (W > m)
+        m = W;
+    int k = 0;
+    while (((int64_t)1 << k) < m)
+        ++k;
+    return k;
+}
+
+uint64_t oracle_hilbert_index(int k, int64_t t, int64_t y, int64_t x)
+{
+    if (k == 0)
+        return 0;
+    uint64_t X[3] = {(uint64_t)t, (uint64_t)y, (uint64_t)x};
+    /* Walk the levels from the top; at each, a set bit of axis i reflects
+     * the lower bits of axis 0, a clear bit swaps them between axes 0 and i. */
+    for (uint64_t Q = (uint64_t)1 << (k - 1); Q > 1; Q >>= 1) {
+        uint64_t low = Q - 1;
+        for (int i = 0; i < 3; ++i) {
+            if (X[i] & Q) {
+                X[0] ^= low;
+            } else {
+                uint64_t d = (X[0] ^ X[i]) & low;
+                X[0] ^= d;
+                X[i] ^= d;
+            }
+        }
+    }
+    /* Gray-code step across the axes, then the correction of the lower bits. */
+    X[1] ^= X[0];
+    X[2] ^= X[1];
+    uint64_t flip = 0;
+    for (uint64_t Q = (uint64_t)1 << (k - 1); Q > 1; Q >>= 1)
+        if (X[2] & Q)
+            flip ^= Q - 1;
+    for (int i = 0; i < 3; ++i)
+        X[i] ^= flip;
+    uint64_t h = 0;
+    for (int b = k - 1; b >= 0; --b)
+        for (int i = 0; i < 3; ++i)
+            h = (h << 1) | ((X[i] >> b) & 1);
+    return h;
+}
+
+typedef struct {
+    uint64_t key;
+    int64_t token;
+} keyed_token;
+
+static int cmp_keyed(const void *pa, const void *pb)
+{
+    const keyed_token *a = (const keyed_token *)pa, *b = (const keyed_token *)pb;
+    return a->key < b->key ? -1 : a->key > b->key ? 1 : 0;
+}
+
+/* seq[r] = raster token of Hilbert rank r, for r in [0, T H W). */
+void oracle_hilbert_order(int64_t T, int64_t H, int64_t W, int64_t *seq)
+{
+    int64_t N = T * H * W;
+    int k = cube_order(T, H, W);
+    keyed_token *kt = (keyed_token *)malloc(sizeof(keyed_token) * (size_t)N);
+    for (int64_t n = 0; n < N; ++n) {
+        kt[n].key = oracle_hilbert_index(k, n / (H * W), (n / W) % H, n % W);
+        kt[n].token = n;
+    }
+    qsort(kt, (size_t)N, sizeof(keyed_token), cmp_keyed);
+    for (int64_t r = 0; r < N; ++r)
+        seq[r] = kt[r].token;
+    free(kt);
+}
+
+/*
  * Evaluate dual-window specs into a dense tile mask M[heads][nT][nT].
  * groups holds the groups of head 0, then head 1, ...; groups_per_head[h]
  * of them per head.
