@@ -102,6 +102,58 @@ def cpu_baseline(wl, M, budget_s=15.0):
             "seconds": dt}
 
 
+def topk_order_comparison(sa, wl, q, k, v, density, stream):
+    """Top-k masks at the given tile density, chosen by the GPU selection on
+    each token order (tile boxes, Hilbert runs), then the fused forward's
+    attention stage timed on each.  F_alg = 4 d sum_h c^T M_h c over the
+    selected mask, c the tiles' real token counts."""
+    import torch
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    out = {}
+    for order in ("tiles", "hilbert"):
+        h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, wl.dtype, order=order)
+        L = sa.sparse_attn_layout(h)
+        ob = torch.empty(max(16, sa.sparse_attn_order_bytes(h)), dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_set_order(h, ob)
+        nT, B = L["tiles"], L["tile_volume"]
+        kk = max(1, round(density * nT))
+        ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+        bm = torch.empty((wl.heads, nT, nT), dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_select_topk(h, [kk] * wl.heads, ws, bm)
+        mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_set_mask(h, mb, bitmap=bm)
+        o = torch.empty_like(q)
+        sa.sparse_attn_permute_kv(h, k, v, ws)
+        for _ in range(2):
+            sa.sparse_attn_attend_raster(h, q, o, ws)
+        ev = []
+        for _ in range(5):
+            a, b = E(), E()
+            a.record(stream)
+            sa.sparse_attn_attend_raster(h, q, o, ws)
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        if order == "tiles":
+            c = np.array([min(wl.tile[0], wl.grid[0] - a * wl.tile[0]) * min(wl.tile[1], wl.grid[1] - b * wl.tile[1])
+                          * min(wl.tile[2], wl.grid[2] - e * wl.tile[2])
+                          for a in range(L["tile_grid"][0]) for b in range(L["tile_grid"][1])
+                          for e in range(L["tile_grid"][2])], dtype=np.float64)
+        else:
+            c = np.full(nT, float(B))
+            c[-1] = L["tokens"] - (nT - 1) * B
+        M = bm.cpu().numpy().astype(np.float64)
+        F = 4.0 * wl.head_dim * float(np.einsum("i,hij,j->", c, M, c))
+        out[order] = {"tiles": nT, "k_per_head": kk, "attention_ms": ms,
+                      "tflops": F / (ms * 1e-3) / 1e12, "flops": F}
+        del ws, mb, bm, o
+    out["note"] = ("top-k masks at the workload's tile density chosen on each order's tiles by the "
+                   "GPU selection; attention stage of the fused forward")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,6 +162,8 @@ def main():
     ap.add_argument("--workload", default="wan", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
+    ap.add_argument("--no-order-comparison", action="store_true",
+                    help="skip the tile-box / Hilbert-order top-k comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration runs)")
     args = ap.parse_args()
@@ -233,6 +287,10 @@ def main():
     select_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
     del sel_bitmap
 
+    orders = None
+    if not args.no_order_comparison:
+        orders = topk_order_comparison(sa, wl, q, k, v, info["tile_density"], stream)
+
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -284,6 +342,7 @@ def main():
                            "pool_gbs": 2 * in_bytes / (select_ms * 1e-3) / 1e9,
                            "note": "top-k over mean-pooled tile scores from the permuted Q, K; "
                                    "not part of the timed step"},
+        "topk_by_token_order": orders,
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -34,6 +34,9 @@ SPARSE_ATTN_BAD_MASK = 3
 SPARSE_ATTN_WORKSPACE_TOO_SMALL = 4
 SPARSE_ATTN_NO_MASK = 5
 SPARSE_ATTN_HIP_ERROR = 6
+SPARSE_ATTN_NO_ORDER = 7
+SPARSE_ATTN_ORDER_TILES = 0
+SPARSE_ATTN_ORDER_HILBERT = 1
 
 SPARSE_ATTN_F32 = 0
 SPARSE_ATTN_BF16 = 1
@@ -47,7 +50,8 @@ SPARSE_ATTN_MAX_GROUPS = 8
 
 EXPORTED = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_layout", "sparse_attn_mask_bytes",
-    "sparse_attn_workspace_bytes", "sparse_attn_set_mask", "sparse_attn_forward",
+    "sparse_attn_workspace_bytes", "sparse_attn_order_bytes", "sparse_attn_set_order",
+    "sparse_attn_set_mask", "sparse_attn_forward",
     "sparse_attn_forward_lse", "sparse_attn_permute_kv", "sparse_attn_attend_raster",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
@@ -59,7 +63,8 @@ EXPORTED = [
 class sparse_attn_config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("grid", ctypes.c_int32 * 3), ("tile", ctypes.c_int32 * 3),
-                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float)]
+                ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+                ("order", ctypes.c_int32)]
 
 
 class sparse_attn_window_group(ctypes.Structure):
@@ -80,7 +85,8 @@ class sparse_attn_layout_info(ctypes.Structure):
                 ("ws_offset_q", ctypes.c_size_t), ("ws_offset_k", ctypes.c_size_t),
                 ("ws_offset_v", ctypes.c_size_t), ("ws_offset_o", ctypes.c_size_t),
                 ("ws_bytes", ctypes.c_size_t), ("pair_axis", ctypes.c_int32),
-                ("pair_grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int64)]
+                ("pair_grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int64),
+                ("order", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -91,6 +97,8 @@ _sigs = {
     "sparse_attn_layout": ([_vp, _P(sparse_attn_layout_info)], ctypes.c_int),
     "sparse_attn_mask_bytes": ([_vp, _i64, _P(_sz)], ctypes.c_int),
     "sparse_attn_workspace_bytes": ([_vp, _P(_sz)], ctypes.c_int),
+    "sparse_attn_order_bytes": ([_vp, _P(_sz)], ctypes.c_int),
+    "sparse_attn_set_order": ([_vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_set_mask": ([_vp, _P(sparse_attn_mask), _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_forward_lse": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -173,12 +181,17 @@ def _nbytes(t):
     return t.numel() * t.element_size()
 
 
-def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0):
-    """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32."""
+def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0,
+                       order=SPARSE_ATTN_ORDER_TILES):
+    """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32; order:
+    "tiles"/"hilbert" or SPARSE_ATTN_ORDER_*."""
     if isinstance(dtype, str):
         dtype = {"bf16": SPARSE_ATTN_BF16, "f32": SPARSE_ATTN_F32}[dtype]
+    if isinstance(order, str):
+        order = {"tiles": SPARSE_ATTN_ORDER_TILES, "hilbert": SPARSE_ATTN_ORDER_HILBERT}[order]
     cfg = sparse_attn_config(int(heads), int(head_dim), (ctypes.c_int32 * 3)(*grid),
-                             (ctypes.c_int32 * 3)(*tile), int(dtype), float(softmax_scale))
+                             (ctypes.c_int32 * 3)(*tile), int(dtype), float(softmax_scale),
+                             int(order))
     out = _vp()
     st = _lib.sparse_attn_create(ctypes.byref(cfg), ctypes.byref(out))
     if st != SPARSE_ATTN_OK:
@@ -209,6 +222,20 @@ def sparse_attn_workspace_bytes(h):
     n = _sz()
     _check(_lib.sparse_attn_workspace_bytes(h.ptr, ctypes.byref(n)), h)
     return n.value
+
+
+def sparse_attn_order_bytes(h):
+    n = _sz()
+    _check(_lib.sparse_attn_order_bytes(h.ptr, ctypes.byref(n)), h)
+    return n.value
+
+
+def sparse_attn_set_order(h, order_buf, stream=None):
+    """Upload the Hilbert rank -> token map into order_buf (device tensor of
+    at least sparse_attn_order_bytes bytes; kept alive by the caller)."""
+    _check(_lib.sparse_attn_set_order(h.ptr, _dptr(order_buf, "order_buf"),
+                                      _nbytes(order_buf) if order_buf is not None else 0,
+                                      _stream(stream)), h)
 
 
 def sparse_attn_set_mask(h, mask_buf, bitmap=None, groups=None, groups_per_head=None, max_nnz=0,

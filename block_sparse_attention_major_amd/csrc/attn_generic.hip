@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
 
     // Row of this slot's query in q and o: the raster token (raster I/O) or
     // the tile-major slot.
-    const int tok = (active && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const int tok = (active && (P.raster || P.lse)) ? raster_token(L, i, slot) : 0;
     const long long qrow = P.raster ? (long long)h * L.N + tok : (long long)h * L.Npad + (long long)i * L.B + slot;
     float q[DH], o[DH];
 #pragma unroll

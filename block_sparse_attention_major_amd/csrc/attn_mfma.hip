@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     // (raster I/O, real slots only) or the tile-major slot.
     const int slot = sub * 32 + l32;
     const bool q_real = slot < ci;
-    const int tok = (q_real && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const int tok = (q_real && (P.raster || P.lse)) ? raster_token(L, i, slot) : 0;
     const long long qrow = P.raster ? (long long)h * L.N + tok
                                     : (long long)h * L.Npad + (long long)max(i, 0) * kTile + slot;
     const bool q_io = wave_active && (q_real || !P.raster);

@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
     // (raster I/O, real slots only) or the tile-major slot.
     const int slot = wave * 32 + l32;
     const bool q_real = slot < ci;
-    const int tok = (q_real && (P.raster || P.lse)) ? slot_token(L, tile_box(L, i), slot) : 0;
+    const int tok = (q_real && (P.raster || P.lse)) ? raster_token(L, i, slot) : 0;
     const long long qrow = P.raster ? (long long)h * L.N + tok
                                     : (long long)h * L.Npad + (long long)i * kTile + slot;
     const bool q_io = q_real || !P.raster;

@@ -33,6 +33,11 @@ struct Layout {
     int pax;
     int pn[3];        // pair grid (tile grid with the paired axis halved)
     int nP;           // pairs per head
+    // Hilbert order: the token grid above is the 1 x 1 x N sequence of
+    // tokens in Hilbert rank order, cut into tiles of 1 x 1 x B, and
+    // seq_tok[p] (device, [N]) is the raster token at sequence position p.
+    // Null for the tile-box order, where positions are raster tokens.
+    const int *seq_tok;
 };
 
 // Clipped extents of tile tau along t, y, x.
@@ -59,13 +64,24 @@ __host__ __device__ inline int tile_real_count(const Layout &L, int tau)
     return r.et * r.ey * r.ex;
 }
 
-// Raster token id of real slot s (0 <= s < c_tau) of the tile with box bx.
+// Grid position of real slot s (0 <= s < c_tau) of the tile with box bx:
+// the raster token in the tile-box order, the sequence position in the
+// Hilbert order.
 __host__ __device__ inline int slot_token(const Layout &L, const TileBox &bx, int s)
 {
     const int plane = bx.ey * bx.ex;
     const int lt = s / plane, rem = s - lt * plane;
     const int ly = rem / bx.ex, lx = rem - ly * bx.ex;
     return ((bx.a * L.tt + lt) * L.H + bx.b * L.th + ly) * L.W + bx.e * L.tw + lx;
+}
+
+// Raster token of grid position p (see Layout::seq_tok).
+__device__ inline int position_token(const Layout &L, int p) { return L.seq_tok ? L.seq_tok[p] : p; }
+
+// Raster token of real slot s of tile tau.
+__device__ inline int raster_token(const Layout &L, int tau, int s)
+{
+    return position_token(L, slot_token(L, tile_box(L, tau), s));
 }
 
 // The query tiles of pair pr (raster over the pair grid); t2 = -1 when the

@@ -3,8 +3,10 @@
 // A tile's real tokens are et * ey runs of ex tokens that are contiguous in
 // raster order, and land in contiguous slots.  So one workgroup per
 // (head, tile) copies each run as one contiguous block of 16-byte vectors:
-// no per-element index arithmetic, fully coalesced reads and writes.  Both
-// kernels are bound by HBM bandwidth.
+// no per-element index arithmetic, fully coalesced reads and writes.  In the
+// Hilbert order each slot's row is fetched from its own raster position
+// (whole rows, still 16-byte vectors).  Both kernels are bound by HBM
+// bandwidth.
 #include "common.h"
 
 namespace sa {
@@ -32,15 +34,30 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(Layout L, int vp
     const TileBox bx = tile_box(L, tau);
     const long long raster0 = (long long)h * L.N;
     const long long slot0 = (long long)h * L.Npad + (long long)tau * L.B;
-    for (int lt = 0; lt < bx.et; ++lt) {
-        for (int ly = 0; ly < bx.ey; ++ly) {
-            const int t = bx.a * L.tt + lt, y = bx.b * L.th + ly, x = bx.e * L.tw;
-            const long long n0 = raster0 + ((long long)t * L.H + y) * L.W + x;
-            const long long p0 = slot0 + (long long)(lt * bx.ey + ly) * bx.ex;
+    if (L.seq_tok) {
+        // Hilbert order: consecutive slots hold tokens scattered over the
+        // raster, so each slot row is copied on its own (still 16-byte
+        // vectors, whole rows per group of threads).
+        const int c = bx.et * bx.ey * bx.ex;
+        for (int u = threadIdx.x; u < c * vpr; u += kThreads) {
+            const int s = u / vpr, w = u - s * vpr;
+            const long long n = raster0 + L.seq_tok[slot_token(L, bx, s)];
             if (DIR == 0)
-                copy_run(src + n0 * vpr, dst + p0 * vpr, bx.ex * vpr);
+                dst[(slot0 + s) * vpr + w] = src[n * vpr + w];
             else
-                copy_run(src + p0 * vpr, dst + n0 * vpr, bx.ex * vpr);
+                dst[n * vpr + w] = src[(slot0 + s) * vpr + w];
+        }
+    } else {
+        for (int lt = 0; lt < bx.et; ++lt) {
+            for (int ly = 0; ly < bx.ey; ++ly) {
+                const int t = bx.a * L.tt + lt, y = bx.b * L.th + ly, x = bx.e * L.tw;
+                const long long n0 = raster0 + ((long long)t * L.H + y) * L.W + x;
+                const long long p0 = slot0 + (long long)(lt * bx.ey + ly) * bx.ex;
+                if (DIR == 0)
+                    copy_run(src + n0 * vpr, dst + p0 * vpr, bx.ex * vpr);
+                else
+                    copy_run(src + p0 * vpr, dst + n0 * vpr, bx.ex * vpr);
+            }
         }
     }
     if (DIR == 0) {
@@ -72,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void permute_tile_columns_kernel(
         const int slot = u / WPR, w = u - slot * WPR;
         uint32_t val = 0;
         if (slot < c) {
-            const long long n = slot_token(L, bx, slot);
+            const long long n = position_token(L, slot_token(L, bx, slot));
             val = reinterpret_cast<const uint32_t *>(src + ((long long)h * L.N + n) * D)[w];
         }
         tileT[slot * LD + 2 * w] = (uint16_t)(val & 0xFFFF);

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -25,6 +26,10 @@ struct sparse_attn_handle {
     sa::MaskBuffers pb{};  // pair lists (matrix-core kernel only; R = 0 otherwise)
     // host copy of the last dual-window spec (source of the upload)
     std::vector<int32_t> spec;
+    // Hilbert order: raster token of each sequence position (host copy, the
+    // source of sparse_attn_set_order's upload)
+    std::vector<int32_t> seq;
+    bool has_order = false;
     std::string err;
 };
 
@@ -142,13 +147,70 @@ int check_ws(sparse_attn_handle *h, const void *ws, size_t ws_bytes)
     return SPARSE_ATTN_OK;
 }
 
+// Checks a caller tensor in raster token order (every call that takes one
+// moves tokens between the raster and the tiles, which in the Hilbert order
+// needs the uploaded sequence map).
 int check_io(sparse_attn_handle *h, const void *p, const char *name)
 {
     if (!p)
         return fail(h, SPARSE_ATTN_INVALID_ARG, "%s is null", name);
     if (!aligned16(p))
         return fail(h, SPARSE_ATTN_INVALID_ARG, "%s is not 16-byte aligned", name);
+    if (h->cfg.order == SPARSE_ATTN_ORDER_HILBERT && !h->has_order)
+        return fail(h, SPARSE_ATTN_NO_ORDER, "the Hilbert order needs sparse_attn_set_order first");
     return SPARSE_ATTN_OK;
+}
+
+// Index of cell (t, y, x) on the 3D Hilbert curve over a 2^k cube, after
+// J. Skilling, "Programming the Hilbert curve", AIP Conf. Proc. 707 (2004):
+// the axes (t, y, x) are turned into the transposed Hilbert index (undo the
+// reflections and exchanges level by level from the top, Gray-encode across
+// the axes, correct the lower bits), whose bits are read level by level
+// from the top, t's first.
+uint64_t hilbert_key(int k, uint32_t t, uint32_t y, uint32_t x)
+{
+    uint32_t c[3] = {t, y, x};
+    for (int lvl = k - 1; lvl >= 1; --lvl) {
+        const uint32_t bit = 1u << lvl, below = bit - 1;
+        for (int a = 0; a < 3; ++a) {
+            if (c[a] & bit) {
+                c[0] ^= below;
+            } else {
+                const uint32_t swap = (c[0] ^ c[a]) & below;
+                c[0] ^= swap;
+                c[a] ^= swap;
+            }
+        }
+    }
+    for (int a = 1; a < 3; ++a)
+        c[a] ^= c[a - 1];
+    uint32_t fix = 0;
+    for (int lvl = k - 1; lvl >= 1; --lvl)
+        if (c[2] & (1u << lvl))
+            fix ^= (1u << lvl) - 1;
+    uint64_t key = 0;
+    for (int lvl = k - 1; lvl >= 0; --lvl)
+        for (int a = 0; a < 3; ++a)
+            key = (key << 1) | (((c[a] ^ fix) >> lvl) & 1u);
+    return key;
+}
+
+// Raster tokens of a T x H x W grid in Hilbert rank order: cells ranked by
+// their index on the curve over the smallest enclosing 2^k cube.
+std::vector<int32_t> hilbert_sequence(int T, int H, int W, int k)
+{
+    const long long N = (long long)T * H * W;
+    std::vector<std::pair<uint64_t, int32_t>> keyed(N);
+    for (long long n = 0; n < N; ++n) {
+        const uint32_t t = uint32_t(n / ((long long)H * W)), y = uint32_t((n / W) % H),
+                       x = uint32_t(n % W);
+        keyed[n] = {hilbert_key(k, t, y, x), int32_t(n)};
+    }
+    std::sort(keyed.begin(), keyed.end());
+    std::vector<int32_t> seq(N);
+    for (long long r = 0; r < N; ++r)
+        seq[r] = keyed[r].second;
+    return seq;
 }
 
 sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
@@ -197,6 +259,7 @@ const char *sparse_attn_status_string(int status)
     case SPARSE_ATTN_BAD_MASK: return "malformed mask";
     case SPARSE_ATTN_WORKSPACE_TOO_SMALL: return "buffer too small";
     case SPARSE_ATTN_NO_MASK: return "no mask set";
+    case SPARSE_ATTN_NO_ORDER: return "no Hilbert sequence set";
     case SPARSE_ATTN_HIP_ERROR: return "HIP runtime error";
     default: return "unknown status";
     }
@@ -228,16 +291,38 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     const long long B = (long long)c.tile[0] * c.tile[1] * c.tile[2];
     if (B > 128)
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "tile volume %lld exceeds 128", B);
+    if (c.order != SPARSE_ATTN_ORDER_TILES && c.order != SPARSE_ATTN_ORDER_HILBERT)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "order must be TILES or HILBERT");
+    const long long N0 = (long long)c.grid[0] * c.grid[1] * c.grid[2];
+    if (N0 >= (1ll << 31))
+        return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "%lld tokens do not fit 32-bit token ids", N0);
+    int cube_k = 0;
+    while ((1ll << cube_k) < std::max({c.grid[0], c.grid[1], c.grid[2]}))
+        ++cube_k;
+    if (c.order == SPARSE_ATTN_ORDER_HILBERT && cube_k > 21)
+        return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "the Hilbert order takes grid sides up to 2^21");
 
     sa::Layout L{};
-    L.T = c.grid[0];
-    L.H = c.grid[1];
-    L.W = c.grid[2];
-    // A tile larger than the grid is allowed: it is clipped like any edge
-    // tile and keeps B = tt th tw slots.
-    L.tt = c.tile[0];
-    L.th = c.tile[1];
-    L.tw = c.tile[2];
+    if (c.order == SPARSE_ATTN_ORDER_TILES) {
+        L.T = c.grid[0];
+        L.H = c.grid[1];
+        L.W = c.grid[2];
+        // A tile larger than the grid is allowed: it is clipped like any
+        // edge tile and keeps B = tt th tw slots.
+        L.tt = c.tile[0];
+        L.th = c.tile[1];
+        L.tw = c.tile[2];
+    } else {
+        // Hilbert order: the tokens in rank order form a 1 x 1 x N grid cut
+        // into tiles of 1 x 1 x B (the last one clipped).
+        L.T = 1;
+        L.H = 1;
+        L.W = (int)N0;
+        L.tt = 1;
+        L.th = 1;
+        L.tw = (int)B;
+    }
+    L.seq_tok = nullptr;
     L.nt = (L.T + L.tt - 1) / L.tt;
     L.ny = (L.H + L.th - 1) / L.th;
     L.nx = (L.W + L.tw - 1) / L.tw;
@@ -274,6 +359,8 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     auto *h = new sparse_attn_handle();
     h->cfg = c;
     h->L = L;
+    if (c.order == SPARSE_ATTN_ORDER_HILBERT)
+        h->seq = hilbert_sequence(c.grid[0], c.grid[1], c.grid[2], cube_k);
     h->elem_bytes = c.dtype == SPARSE_ATTN_F32 ? 4 : 2;
     h->kernel = (c.dtype == SPARSE_ATTN_BF16 && B == 128) ? SPARSE_ATTN_KERNEL_MFMA_BF16
                                                           : SPARSE_ATTN_KERNEL_GENERIC;
@@ -308,6 +395,36 @@ int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *inf
     for (int a = 0; a < 3; ++a)
         info->pair_grid[a] = h->L.pn[a];
     info->pairs = h->L.nP;
+    info->order = h->cfg.order;
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_order_bytes(const sparse_attn_handle *h, size_t *bytes)
+{
+    if (!h || !bytes)
+        return SPARSE_ATTN_INVALID_ARG;
+    *bytes = 4 * h->seq.size();
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_set_order(sparse_attn_handle *h, void *order_buf, size_t bytes, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (h->cfg.order != SPARSE_ATTN_ORDER_HILBERT)
+        return SPARSE_ATTN_OK;
+    if (!order_buf || !aligned16(order_buf))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "order_buf must be non-null and 16-byte aligned");
+    const size_t need = 4 * h->seq.size();
+    if (bytes < need)
+        return fail(h, SPARSE_ATTN_WORKSPACE_TOO_SMALL, "order buffer holds %zu bytes, %zu needed", bytes,
+                    need);
+    const hipError_t e = hipMemcpyAsync(order_buf, h->seq.data(), need, hipMemcpyHostToDevice,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return hip_fail(h, e, "uploading the Hilbert sequence");
+    h->L.seq_tok = static_cast<const int *>(order_buf);
+    h->has_order = true;
     return SPARSE_ATTN_OK;
 }
 

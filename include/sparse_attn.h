@@ -59,7 +59,8 @@ enum {
     SPARSE_ATTN_BAD_MASK = 3,            /* malformed mask description */
     SPARSE_ATTN_WORKSPACE_TOO_SMALL = 4, /* a caller buffer is smaller than required */
     SPARSE_ATTN_NO_MASK = 5,             /* forward/attend before set_mask */
-    SPARSE_ATTN_HIP_ERROR = 6            /* the HIP runtime reported an error */
+    SPARSE_ATTN_HIP_ERROR = 6,           /* the HIP runtime reported an error */
+    SPARSE_ATTN_NO_ORDER = 7             /* Hilbert order without sparse_attn_set_order */
 };
 
 /* Element types of Q, K, V and O. */
@@ -83,6 +84,29 @@ enum {
     SPARSE_ATTN_KERNEL_GENERIC = 1    /* fp32 vector-ALU kernel: any supported shape */
 };
 
+/*
+ * Token orders (sparse_attn_config.order): which tokens form a tile.
+ *
+ * TILES: tiles are tt x th x tw boxes of the grid, numbered raster over the
+ * tile grid (t, then y, then x); edge tiles are clipped.
+ *
+ * HILBERT: tokens are ranked along a 3D Hilbert curve and tiles are runs of
+ * B = tt th tw consecutive ranks (DFSAttn page, abstract: Hilbert-curve
+ * token reordering keeps blocks spatially compact at a finer grain than
+ * boxes).  The curve is J. Skilling's ("Programming the Hilbert curve",
+ * AIP Conf. Proc. 707, 2004) over the smallest cube of side 2^k holding
+ * the grid, axes (t, y, x), its index bits read level by level from the
+ * top with t's first; cube cells outside the grid are skipped.  Everything
+ * that describes tiles then describes a 1 x 1 x N grid of tokens in rank
+ * order cut into 1 x 1 x B tiles: nT = ceil(N / B), tile_grid = (1, 1, nT),
+ * only the last tile is clipped, and a dual-window group reduces to a band
+ * |i - j| <= rx[w] of tiles along the curve.  The rank -> token map lives in
+ * a caller-owned device buffer (sparse_attn_order_bytes /
+ * sparse_attn_set_order); results do not depend on the order, only which
+ * tokens share a tile does.
+ */
+enum { SPARSE_ATTN_ORDER_TILES = 0, SPARSE_ATTN_ORDER_HILBERT = 1 };
+
 /* Maximum temporal-distance groups per head in a dual-window mask. */
 #define SPARSE_ATTN_MAX_GROUPS 8
 
@@ -93,6 +117,7 @@ typedef struct sparse_attn_config {
     int32_t tile[3];       /* tt, th, tw: tile shape, each >= 1, product B <= 128 */
     int32_t dtype;         /* SPARSE_ATTN_F32 or SPARSE_ATTN_BF16 */
     float softmax_scale;   /* score scale s; 0 selects 1 / sqrt(head_dim) */
+    int32_t order;         /* SPARSE_ATTN_ORDER_TILES (0) or SPARSE_ATTN_ORDER_HILBERT */
 } sparse_attn_config;
 
 /*
@@ -144,6 +169,7 @@ typedef struct sparse_attn_layout_info {
     int32_t pair_axis;
     int32_t pair_grid[3];
     int64_t pairs;
+    int32_t order;         /* SPARSE_ATTN_ORDER_* of the handle */
 } sparse_attn_layout_info;
 
 typedef struct sparse_attn_handle sparse_attn_handle;
@@ -154,8 +180,9 @@ typedef struct sparse_attn_handle sparse_attn_handle;
  * tiles at the far edges of a grid the tile does not divide are clipped.
  * Each tile owns B consecutive slots: its c real tokens fill the first c in
  * raster order over the clipped tile, the rest are empty.
- * Errors: INVALID_ARG (null, non-positive sizes, bad dtype),
- * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31).
+ * Errors: INVALID_ARG (null, non-positive sizes, bad dtype or order),
+ * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31,
+ * N >= 2^31, a Hilbert grid side above 2^21).
  * On success *out owns host memory only; release it with sparse_attn_destroy.
  */
 int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out);
@@ -175,6 +202,22 @@ int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t 
 /* Device bytes of the forward workspace (permuted Q, K, V and O).
  * Errors: INVALID_ARG. */
 int sparse_attn_workspace_bytes(const sparse_attn_handle *h, size_t *bytes);
+
+/* Device bytes of the token-order buffer: 4 N in the Hilbert order (the
+ * raster token of each rank, int32), 0 in the tile order.
+ * Errors: INVALID_ARG. */
+int sparse_attn_order_bytes(const sparse_attn_handle *h, size_t *bytes);
+
+/*
+ * Hilbert order: upload the rank -> token map into order_buf (device,
+ * caller-owned, 16-byte aligned, at least sparse_attn_order_bytes bytes),
+ * which must stay alive and unmodified while the handle moves tokens.
+ * Every call that takes a tensor in raster order (forward, the permute and
+ * attend stages, the permute hooks) fails with NO_ORDER until this is done.
+ * In the tile order it does nothing and succeeds.
+ * Errors: INVALID_ARG, WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int sparse_attn_set_order(sparse_attn_handle *h, void *order_buf, size_t bytes, void *stream);
 
 /*
  * Compile a mask on the GPU into mask_buf: per query-tile row r = h nT + i

@@ -88,6 +88,7 @@ def test_pair_axis_choice(sa, grid, axis, pgrid):
     (dict(heads=0), 1), (dict(grid=(0, 8, 8)), 1), (dict(tile=(1, 0, 4)), 1),
     (dict(dtype=7), 1), (dict(softmax_scale=-1.0), 1), (dict(softmax_scale=float("inf")), 1),
     (dict(head_dim=96), 2), (dict(tile=(2, 8, 16)), 2), (dict(grid=(400, 64, 64), tile=(1, 1, 1)), 2),
+    (dict(order=5), 1), (dict(grid=(4, 8, 1 << 22), order=1), 2),
 ])
 def test_create_rejects(sa, kw, code):
     args = dict(heads=2, head_dim=64, grid=(4, 8, 8), tile=(1, 4, 4), dtype="f32", softmax_scale=0.0)
@@ -176,7 +177,34 @@ def test_permute_hook_checks(sa):
     assert r(h.ptr, FAKE, FAKE, 10, FAKE, None) == sa.SPARSE_ATTN_NO_MASK
 
 
+def test_hilbert_layout(sa):
+    """Hilbert order: runs of B ranks form a 1 x 1 x nT tile grid, the last
+    tile clipped; the order buffer holds one int32 per token."""
+    h = sa.sparse_attn_create(2, 128, (3, 20, 36), (1, 8, 16), "bf16", order="hilbert")
+    L = sa.sparse_attn_layout(h)
+    N = 3 * 20 * 36
+    assert L["order"] == sa.SPARSE_ATTN_ORDER_HILBERT and L["tokens"] == N
+    assert L["tiles"] == -(-N // 128) and L["tile_grid"] == [1, 1, L["tiles"]]
+    assert L["slots"] == L["tiles"] * 128 and L["pair_axis"] == 2
+    assert sa.sparse_attn_order_bytes(h) == 4 * N
+    t = sa.sparse_attn_create(2, 128, (3, 20, 36), (1, 8, 16), "bf16")
+    assert sa.sparse_attn_layout(t)["order"] == sa.SPARSE_ATTN_ORDER_TILES
+    assert sa.sparse_attn_order_bytes(t) == 0
+    assert sa._lib.sparse_attn_set_order(t.ptr, None, 0, None) == 0  # nothing to do
+
+
+def test_hilbert_calls_need_the_order(sa):
+    h = sa.sparse_attn_create(2, 64, (4, 8, 8), (1, 4, 4), "f32", order="hilbert")
+    st = sa._lib.sparse_attn_forward(h.ptr, FAKE, FAKE + 2**30, FAKE + 2**31, FAKE + 2**32,
+                                     FAKE + 2**33, _ws(sa, h), None)
+    assert st == sa.SPARSE_ATTN_NO_ORDER
+    assert sa._lib.sparse_attn_permute(h.ptr, FAKE, FAKE + 2**30, 0, None) == sa.SPARSE_ATTN_NO_ORDER
+    assert sa._lib.sparse_attn_set_order(h.ptr, FAKE + 8, 1 << 20, None) == sa.SPARSE_ATTN_INVALID_ARG
+    assert sa._lib.sparse_attn_set_order(h.ptr, FAKE, 16, None) == sa.SPARSE_ATTN_WORKSPACE_TOO_SMALL
+
+
 def test_status_strings(sa):
     assert sa.sparse_attn_status_string(0) == "ok"
     assert "mask" in sa.sparse_attn_status_string(sa.SPARSE_ATTN_NO_MASK)
+    assert "Hilbert" in sa.sparse_attn_status_string(sa.SPARSE_ATTN_NO_ORDER)
     assert sa.sparse_attn_status_string(99) == "unknown status"
