@@ -56,6 +56,10 @@ def _load():
         lib.oracle_hilbert_index.restype = ctypes.c_uint64
         lib.oracle_hilbert_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_void_p]
+        lib.oracle_tile_mass.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_double,
+                                         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                         ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -229,3 +233,25 @@ def flops(M, counts, d):
     """Algorithmic FLOPs 4 d sum over kept tile pairs of c_i c_j."""
     c = np.asarray(counts, dtype=np.float64)
     return 4.0 * d * sum(float(c @ (M[h] != 0).astype(np.float64) @ c) for h in range(M.shape[0]))
+
+
+def tile_mass(grid, tile, q, k, qtiles=None, scale=None, threads=None):
+    """Full-attention mass per tile pair, fp64: A[h, i, j] = mean over the
+    real queries of tile i of the softmax mass (over all keys) on tile j.
+    qtiles: flattened h * nT + i to evaluate (default all) -> [len, nT];
+    with qtiles None the result is [heads, nT, nT]."""
+    q = np.ascontiguousarray(q)
+    k = np.ascontiguousarray(k)
+    heads, N, d = q.shape
+    if _dtype_code(k) != _dtype_code(q):
+        raise TypeError("q, k must share a dtype")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nT = num_tiles(grid, tile)
+    full = qtiles is None
+    qt = np.arange(heads * nT, dtype=np.int64) if full else np.ascontiguousarray(qtiles, dtype=np.int64)
+    out = np.empty((len(qt), nT), dtype=np.float64)
+    _load().oracle_tile_mass(ctypes.byref(_grid(grid, tile)), heads, d, _dtype_code(q), _ptr(q),
+                             _ptr(k), float(scale), _ptr(qt), len(qt), _ptr(out),
+                             int(threads or default_threads()))
+    return out.reshape(heads, nT, nT) if full else out

@@ -498,3 +498,69 @@ void oracle_select_topk(const oracle_grid *g, int64_t heads, int64_t d, int dtyp
     free(qb);
     free(kb);
 }
+
+/*
+ * Reference attention mass per tile pair, the quantity the offline mask
+ * search works on (Compact Attention page, Fig. 1 caption: reference
+ * attention mass of query-key regions; Fig. 4 caption: the search keeps the
+ * regions that hold most of each head's attention mass).  The reference is
+ * full attention: for query token n of head h,
+ *     p(n, m) = exp(s q_n.k_m - mu_n) / sum_{m' < N} exp(s q_n.k_m' - mu_n)
+ * over all N keys, and for query tile i, key tile j
+ *     A[h][i][j] = (1 / c_i) sum_{n in tile i} sum_{m in tile j} p(n, m),
+ * the mean over the tile's real queries of the mass they give tile j.
+ * Only the query tiles listed in qtiles[count] (flattened h nT + i) are
+ * evaluated: out[count][nT].
+ */
+void oracle_tile_mass(const oracle_grid *g, int64_t heads, int64_t d, int dtype, const void *q,
+                      const void *k, double scale, const int64_t *qtiles, int64_t count, double *out,
+                      int nthreads)
+{
+    int64_t N = g->T * g->H * g->W;
+    int64_t nT = oracle_num_tiles(g);
+    int64_t *tile = (int64_t *)malloc(sizeof(int64_t) * (size_t)N);
+    int64_t *cnt = (int64_t *)calloc((size_t)nT, sizeof(int64_t));
+    for (int64_t n = 0; n < N; ++n) {
+        tile[n] = tile_of_token(g, n);
+        cnt[tile[n]] += 1;
+    }
+    (void)heads;
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#pragma omp parallel
+    {
+        double *score = (double *)malloc(sizeof(double) * (size_t)N);
+        double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t c = 0; c < count; ++c) {
+            int64_t h = qtiles[c] / nT, i = qtiles[c] % nT;
+            double *row = out + c * nT;
+            for (int64_t j = 0; j < nT; ++j)
+                row[j] = 0.0;
+            for (int64_t n = 0; n < N; ++n) {
+                if (tile[n] != i)
+                    continue;
+                for (int64_t e = 0; e < d; ++e)
+                    qrow[e] = load_elem(q, dtype, (h * N + n) * d + e);
+                double mu = -INFINITY;
+                for (int64_t m = 0; m < N; ++m) {
+                    double dot = 0.0;
+                    for (int64_t e = 0; e < d; ++e)
+                        dot += qrow[e] * load_elem(k, dtype, (h * N + m) * d + e);
+                    score[m] = scale * dot;
+                    if (score[m] > mu)
+                        mu = score[m];
+                }
+                double den = 0.0;
+                for (int64_t m = 0; m < N; ++m)
+                    den += exp(score[m] - mu);
+                for (int64_t m = 0; m < N; ++m)
+                    row[tile[m]] += exp(score[m] - mu) / den / (double)cnt[i];
+            }
+        }
+        free(score);
+        free(qrow);
+    }
+    free(tile);
+    free(cnt);
+}
