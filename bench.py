@@ -154,6 +154,57 @@ def topk_order_comparison(sa, wl, q, k, v, density, stream):
     return out
 
 
+def window_search(sa, wl, q, k, v, stream, tau=0.9):
+    """The offline search on the workload's inputs: full-attention tile mass
+    on the GPU (timed), the host search at recall tau over the temporal
+    groups {0}, {1-2}, {>= 3}, and the attention stage of the fused forward
+    under the searched mask."""
+    import torch
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, wl.dtype)
+    L = sa.sparse_attn_layout(h)
+    nT, N, d = L["tiles"], L["tokens"], wl.head_dim
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    mass = torch.empty((wl.heads, nT, nT), dtype=torch.float32, device="cuda")
+    sa.sparse_attn_tile_mass(h, q, k, ws, mass)
+    a, b = E(), E()
+    a.record(stream)
+    sa.sparse_attn_tile_mass(h, q, k, ws, mass)
+    b.record(stream)
+    torch.cuda.synchronize()
+    mass_ms = a.elapsed_time(b)
+    A = mass.cpu().numpy()
+    spec = [(0, 0), (1, 2), (3, -1)]
+    g_in = np.array([(lo, hi, 0, 0, 0, 0) for lo, hi in spec] * wl.heads, np.int32)
+    gph = np.full(wl.heads, len(spec), np.int32)
+    t0 = time.perf_counter()
+    groups, rec, cost = sa.sparse_attn_search_windows(h, A, g_in, gph, tau)
+    search_s = time.perf_counter() - t0
+    mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+    sa.sparse_attn_set_mask(h, mb, groups=groups, groups_per_head=gph)
+    o = torch.empty_like(q)
+    sa.sparse_attn_permute_kv(h, k, v, ws)
+    for _ in range(2):
+        sa.sparse_attn_attend_raster(h, q, o, ws)
+    ev = []
+    for _ in range(5):
+        a, b = E(), E()
+        a.record(stream)
+        sa.sparse_attn_attend_raster(h, q, o, ws)
+        b.record(stream)
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    F_mass = 2 * 2.0 * d * float(N) * float(N) * wl.heads  # two passes of Q K^T over all pairs
+    F_attn = 4.0 * d * float(N) * float(N) * wl.heads * float(cost.mean())
+    return {"tau": tau, "mass_ms": mass_ms, "mass_tflops": F_mass / (mass_ms * 1e-3) / 1e12,
+            "search_s": search_s, "recall_mean": float(rec.mean()), "recall_min": float(rec.min()),
+            "token_density_mean": float(cost.mean()), "attention_ms": attn_ms,
+            "attention_tflops": F_attn / (attn_ms * 1e-3) / 1e12,
+            "note": "tile mass of full attention on the GPU (both passes, with the Q/K permute), "
+                    "host greedy dual-window search per head, attention stage under the searched mask"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +213,7 @@ def main():
     ap.add_argument("--workload", default="wan", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
+    ap.add_argument("--no-search", action="store_true", help="skip the window-search measurement")
     ap.add_argument("--no-order-comparison", action="store_true",
                     help="skip the tile-box / Hilbert-order top-k comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -287,6 +339,9 @@ def main():
     select_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
     del sel_bitmap
 
+    searched = None
+    if not args.no_search:
+        searched = window_search(sa, wl, q, k, v, stream)
     orders = None
     if not args.no_order_comparison:
         orders = topk_order_comparison(sa, wl, q, k, v, info["tile_density"], stream)
@@ -343,6 +398,7 @@ def main():
                            "note": "top-k over mean-pooled tile scores from the permuted Q, K; "
                                    "not part of the timed step"},
         "topk_by_token_order": orders,
+        "window_search": searched,
     }
     if not args.no_cpu_baseline:
         import oracle

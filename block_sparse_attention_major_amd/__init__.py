@@ -55,7 +55,8 @@ EXPORTED = [
     "sparse_attn_forward_lse", "sparse_attn_permute_kv", "sparse_attn_attend_raster",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
-    "sparse_attn_read_pair_lists", "sparse_attn_select_topk",
+    "sparse_attn_read_pair_lists", "sparse_attn_select_topk", "sparse_attn_tile_mass",
+    "sparse_attn_search_windows",
     "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
 ]
 
@@ -112,6 +113,9 @@ _sigs = {
     "sparse_attn_read_index_lists": ([_vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
     "sparse_attn_read_pair_lists": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_select_topk": ([_vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    "sparse_attn_tile_mass": ([_vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    "sparse_attn_search_windows": ([_vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp, _vp,
+                                    _vp], ctypes.c_int),
     "sparse_attn_mask_info": ([_vp, _P(_i64), _P(_i32), _vp], ctypes.c_int),
     "sparse_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sparse_attn_last_error": ([_vp], ctypes.c_char_p),
@@ -367,3 +371,26 @@ class SparseAttention:
             o = self.torch.empty_like(q)
         sparse_attn_forward(self.h, q, k, v, o, self.ws, stream)
         return o
+
+
+def sparse_attn_tile_mass(h, q, k, ws, mass, stream=None):
+    """Full-attention mass per tile pair into mass (device fp32 [heads, nT, nT])."""
+    _check(_lib.sparse_attn_tile_mass(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(ws, "ws"), _nbytes(ws),
+                                      _dptr(mass, "mass"), _stream(stream)), h)
+
+
+def sparse_attn_search_windows(h, mass, groups, groups_per_head, tau, lam=float("inf")):
+    """Host search.  mass: host float32 [heads, nT, nT]; groups: int32 [G, 6]
+    rows (dt_lo, dt_hi, ...) (windows ignored); returns (groups [G, 6] with
+    the searched windows, recall [heads], cost [heads])."""
+    m = np.ascontiguousarray(mass, dtype=np.float32)
+    g = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 6)
+    gph = np.ascontiguousarray(groups_per_head, dtype=np.int32)
+    out = np.zeros_like(g)
+    heads = gph.shape[0]
+    rec = np.zeros(heads)
+    cst = np.zeros(heads)
+    _check(_lib.sparse_attn_search_windows(h.ptr, m.ctypes.data, g.ctypes.data, gph.ctypes.data,
+                                           float(tau), float(lam), out.ctypes.data, rec.ctypes.data,
+                                           cst.ctypes.data), h)
+    return out, rec, cst

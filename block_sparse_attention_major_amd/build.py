@@ -18,7 +18,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["sparse_attn.cpp", "permute.hip", "mask.hip", "attn_mfma.hip", "attn_rows.hip",
-           "attn_generic.hip", "select.hip"]
+           "attn_generic.hip", "select.hip", "mass.hip", "search.cpp"]
 
 # Packed fp32 VALU instructions are switched off for every device compile.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

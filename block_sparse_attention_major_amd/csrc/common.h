@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sparse_attn.h"
+
 namespace sa {
 
 struct Layout {
@@ -251,8 +253,19 @@ hipError_t launch_select_topk(const Layout &L, int elem_bytes, const void *q, co
                               const int *kh, float scale, float *qbar, float *kbar, uint8_t *bitmap,
                               hipStream_t s);
 
+// Full-attention mass per tile pair from the tile-major bf16 Q and K (B ==
+// 128): mass [heads][nT][nT], row (h, i) = mean over tile i's real queries
+// of the softmax mass on each key tile.
+hipError_t launch_tile_mass(const Layout &L, const void *q, const void *k, float scale_log2, float *mass,
+                            hipStream_t s);
+
 // fp32 vector-ALU kernel for any supported shape; elem_bytes 4 (fp32) or 2 (bf16).
 hipError_t launch_attention_generic(const Layout &L, int elem_bytes, const AttnParams &p,
                                     hipStream_t s);
+
+// Greedy dual-window search of one head on the host (mass A [nT][nT] fp32;
+// G validated groups; writes G groups with their windows, recall and cost).
+int search_head(const Layout &L, const float *A, const sparse_attn_window_group *gin, int G, double tau,
+                double lambda, sparse_attn_window_group *gout, double *recall, double *cost);
 
 }  // namespace sa

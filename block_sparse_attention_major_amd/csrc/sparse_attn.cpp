@@ -161,6 +161,45 @@ int check_io(sparse_attn_handle *h, const void *p, const char *name)
     return SPARSE_ATTN_OK;
 }
 
+// Validates the temporal-distance groups of a dual-window spec (and, with
+// windows, their half-extents); off gets the per-head group offsets.
+int check_groups(sparse_attn_handle *h, const sparse_attn_window_group *groups, const int32_t *gph,
+                 bool windows, std::vector<int32_t> &off)
+{
+    const int heads = h->L.heads;
+    off.assign(heads + 1, 0);
+    for (int hh = 0; hh < heads; ++hh) {
+        const int ng = gph[hh];
+        if (ng < 1 || ng > SPARSE_ATTN_MAX_GROUPS)
+            return fail(h, SPARSE_ATTN_BAD_MASK, "head %d has %d groups (1..%d allowed)", hh, ng,
+                        SPARSE_ATTN_MAX_GROUPS);
+        off[hh + 1] = off[hh] + ng;
+    }
+    for (int hh = 0; hh < heads; ++hh) {
+        long long prev_hi = -1;
+        for (int g = off[hh]; g < off[hh + 1]; ++g) {
+            const sparse_attn_window_group &G = groups[g];
+            const bool last = g + 1 == off[hh + 1];
+            if (G.dt_lo < 0 || (G.dt_hi < 0 && G.dt_hi != -1) || (G.dt_hi >= 0 && G.dt_hi < G.dt_lo))
+                return fail(h, SPARSE_ATTN_BAD_MASK, "head %d group %d: bad distance range [%d, %d]", hh,
+                            g - off[hh], G.dt_lo, G.dt_hi);
+            if (G.dt_hi == -1 && !last)
+                return fail(h, SPARSE_ATTN_BAD_MASK,
+                            "head %d group %d: an unbounded group must be the last", hh, g - off[hh]);
+            if (G.dt_lo <= prev_hi)
+                return fail(h, SPARSE_ATTN_BAD_MASK,
+                            "head %d group %d: groups must be sorted and disjoint", hh, g - off[hh]);
+            for (int w = 0; windows && w < 2; ++w) {
+                if (G.ry[w] < -1 || G.rx[w] < -1)
+                    return fail(h, SPARSE_ATTN_BAD_MASK,
+                                "head %d group %d window %d: half-extents must be >= -1", hh, g - off[hh], w);
+            }
+            prev_hi = G.dt_hi;
+        }
+    }
+    return SPARSE_ATTN_OK;
+}
+
 // Index of cell (t, y, x) on the 3D Hilbert curve over a 2^k cube, after
 // J. Skilling, "Programming the Hilbert curve", AIP Conf. Proc. 707 (2004):
 // the axes (t, y, x) are turned into the transposed Hilbert index (undo the
@@ -470,38 +509,13 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
     } else if (m->kind == SPARSE_ATTN_MASK_DUAL_WINDOW) {
         if (!m->groups || !m->groups_per_head)
             return fail(h, SPARSE_ATTN_INVALID_ARG, "dual-window mask without groups");
-        std::vector<int32_t> off(L.heads + 1, 0);
-        for (int hh = 0; hh < L.heads; ++hh) {
-            const int ng = m->groups_per_head[hh];
-            if (ng < 1 || ng > SPARSE_ATTN_MAX_GROUPS)
-                return fail(h, SPARSE_ATTN_BAD_MASK, "head %d has %d groups (1..%d allowed)", hh, ng,
-                            SPARSE_ATTN_MAX_GROUPS);
-            off[hh + 1] = off[hh] + ng;
-        }
-        for (int hh = 0; hh < L.heads; ++hh) {
-            long long prev_hi = -1;
-            for (int g = off[hh]; g < off[hh + 1]; ++g) {
-                const sparse_attn_window_group &G = m->groups[g];
-                const bool last = g + 1 == off[hh + 1];
-                if (G.dt_lo < 0 || (G.dt_hi < 0 && G.dt_hi != -1) ||
-                    (G.dt_hi >= 0 && G.dt_hi < G.dt_lo))
-                    return fail(h, SPARSE_ATTN_BAD_MASK, "head %d group %d: bad distance range [%d, %d]",
-                                hh, g - off[hh], G.dt_lo, G.dt_hi);
-                if (G.dt_hi == -1 && !last)
-                    return fail(h, SPARSE_ATTN_BAD_MASK,
-                                "head %d group %d: an unbounded group must be the last", hh, g - off[hh]);
-                if (G.dt_lo <= prev_hi)
-                    return fail(h, SPARSE_ATTN_BAD_MASK,
-                                "head %d group %d: groups must be sorted and disjoint", hh, g - off[hh]);
-                for (int w = 0; w < 2; ++w) {
-                    if (G.ry[w] < -1 || G.rx[w] < -1)
-                        return fail(h, SPARSE_ATTN_BAD_MASK,
-                                    "head %d group %d window %d: half-extents must be >= -1", hh,
-                                    g - off[hh], w);
-                }
-                prev_hi = G.dt_hi;
-                spec.insert(spec.end(), {G.dt_lo, G.dt_hi, G.ry[0], G.ry[1], G.rx[0], G.rx[1]});
-            }
+        std::vector<int32_t> off;
+        int st;
+        if ((st = check_groups(h, m->groups, m->groups_per_head, true, off)))
+            return st;
+        for (int g = 0; g < off[L.heads]; ++g) {
+            const sparse_attn_window_group &G = m->groups[g];
+            spec.insert(spec.end(), {G.dt_lo, G.dt_hi, G.ry[0], G.ry[1], G.rx[0], G.rx[1]});
         }
         spec.insert(spec.end(), off.begin(), off.end());
     } else {
@@ -715,6 +729,62 @@ int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, con
                         void *ws, size_t ws_bytes, void *stream)
 {
     return sparse_attn_forward_lse(h, q, k, v, o, nullptr, ws, ws_bytes, stream);
+}
+
+int sparse_attn_tile_mass(sparse_attn_handle *h, const void *q, const void *k, void *ws,
+                          size_t ws_bytes, float *mass, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, q, "q")) || (st = check_io(h, k, "k")) || (st = check_ws(h, ws, ws_bytes)))
+        return st;
+    if (!mass || !aligned16(mass))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "mass must be non-null and 16-byte aligned");
+    if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "the tile mass runs on the matrix-core path (bf16, B = 128)");
+    const sa::Layout &L = h->L;
+    const size_t n = io_bytes(h), mb = size_t(L.heads) * L.nT * L.nT * sizeof(float);
+    const WsLayout w = ws_layout(h);
+    for (const void *p : {q, k})
+        if (overlaps(p, n, ws, w.total) || overlaps(mass, mb, p, n))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "q, k, mass and the workspace must not overlap");
+    if (overlaps(mass, mb, ws, w.total))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "mass must not overlap the workspace");
+    char *b = static_cast<char *>(ws);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_permute_rows(L, h->elem_bytes, q, b + w.q, s);
+    if (e == hipSuccess)
+        e = sa::launch_permute_rows(L, h->elem_bytes, k, b + w.k, s);
+    if (e == hipSuccess)
+        e = sa::launch_tile_mass(L, b + w.q, b + w.k, h->scale * 1.4426950408889634f, mass, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "tile mass");
+    return SPARSE_ATTN_OK;
+}
+
+int sparse_attn_search_windows(sparse_attn_handle *h, const float *mass,
+                               const sparse_attn_window_group *groups_in, const int32_t *groups_per_head,
+                               double tau, double lambda, sparse_attn_window_group *groups_out,
+                               double *recall, double *cost)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    if (!mass || !groups_in || !groups_per_head || !groups_out || !recall || !cost)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "null argument");
+    if (!(tau >= 0.0 && tau <= 1.0))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "tau must lie in [0, 1]");
+    if (!(lambda > 0.0))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "lambda must be > 0 (infinity disables it)");
+    std::vector<int32_t> off;
+    int st;
+    if ((st = check_groups(h, groups_in, groups_per_head, false, off)))
+        return st;
+    const sa::Layout &L = h->L;
+    for (int hh = 0; hh < L.heads; ++hh)
+        sa::search_head(L, mass + (size_t)hh * L.nT * L.nT, groups_in + off[hh], off[hh + 1] - off[hh], tau,
+                        lambda, groups_out + off[hh], recall + hh, cost + hh);
+    return SPARSE_ATTN_OK;
 }
 
 int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, void *ws,

@@ -304,6 +304,59 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
                             size_t ws_bytes, uint8_t *bitmap, void *stream);
 
 /*
+ * Reference attention mass per tile pair, the input of the offline window
+ * search (Compact Attention page, Fig. 1 caption: reference attention mass
+ * of query-key regions; Fig. 4 caption: the search keeps the regions that
+ * hold most of each head's attention mass).  With p(n, .) the softmax of
+ * s q_n . k over ALL N keys,
+ *     mass[h][i][j] = (1 / c_i) sum_{n in tile i} sum_{m in tile j} p(n, m),
+ * the mean over the real queries of tile i of the mass they give tile j
+ * (each row sums to 1).  q, k: raster [heads][N][head_dim] bf16; ws: the
+ * forward workspace (its Q and K regions are overwritten); mass: device fp32
+ * [heads][nT][nT], out.  This is dense work (two passes of Q K^T over every
+ * key); it is meant for offline calibration, not the forward path.
+ * Errors: INVALID_ARG, UNSUPPORTED (needs the matrix-core path: bf16,
+ * B = 128), WORKSPACE_TOO_SMALL, NO_ORDER, HIP_ERROR.
+ */
+int sparse_attn_tile_mass(sparse_attn_handle *h, const void *q, const void *k, void *ws,
+                          size_t ws_bytes, float *mass, void *stream);
+
+/*
+ * Offline dual-window search on the host (Compact Attention page, Fig. 3
+ * caption: windows shrunk under a recall constraint tau and a cost
+ * constraint lambda; Fig. 4 caption: starting from full coverage in every
+ * temporal-distance group; Fig. 1 caption part (3): two windows per group).
+ * The pages give no formula; this is the reading implemented:
+ *   - Tile pair (i, j) weighs w = round(mass[i][j] c_i 2^24) and costs
+ *     c_i c_j.  A head's recall is its kept weight over all its weight, its
+ *     cost the kept cost over N^2.
+ *   - The groups' [dt_lo, dt_hi] come from groups_in (windows ignored).  A
+ *     group's kept offsets (|db|, |de|) are the union of a wide rectangle
+ *     (ry y, rx X) and a tall one (ry Y, rx x), -1 <= y <= Y <= ny - 1 and
+ *     -1 <= x <= X <= nx - 1: window 0 = (y, X), window 1 = (Y, x).
+ *   - Start: every group full (y = Y = ny - 1, x = X = nx - 1).  Moves of a
+ *     group, numbered: 0 notch a rectangle's corner (y = Y and x = X:
+ *     y -= 1, x -= 1); 1 y -= 1; 2 x -= 1; 3 Y -= 1 (y = min(y, Y));
+ *     4 X -= 1 (x = min(x, X)).  A move that uncovers no offset is not a
+ *     candidate.  A candidate is admissible when the kept weight stays at
+ *     least ceil(tau * total weight) and lost weight / total weight is at
+ *     most lambda * saved cost / N^2 (lambda = INFINITY: no such limit).
+ *   - Each step applies the admissible candidate of any group with the
+ *     least lost weight per saved cost (a move that saves no cost comes
+ *     first), ties to the larger saved cost, the lower group, the lower
+ *     move; the search stops when none is admissible.
+ * mass: host fp32 [heads][nT][nT] (sparse_attn_tile_mass copied back);
+ * groups_in / groups_per_head: as for a dual-window mask; groups_out: host,
+ * same count, the searched windows; recall, cost: host [heads].  Host only,
+ * synchronous.  Errors: INVALID_ARG (null, tau outside [0, 1], lambda <=
+ * 0), BAD_MASK (groups).
+ */
+int sparse_attn_search_windows(sparse_attn_handle *h, const float *mass,
+                               const sparse_attn_window_group *groups_in, const int32_t *groups_per_head,
+                               double tau, double lambda, sparse_attn_window_group *groups_out,
+                               double *recall, double *cost);
+
+/*
  * Test hooks.
  * sparse_attn_permute: src [heads][N][head_dim] raster -> dst in `layout`
  *   (SPARSE_ATTN_LAYOUT_*), empty slots zero.  dst holds heads * nT * B *

@@ -1,0 +1,101 @@
+"""The library's host window search (sparse_attn_search_windows) against the
+oracle's (oracle/search.py) on the same fp32 tile masses: the searched
+windows must be identical and the recall and cost equal (the search's
+decisions use integer weights, so both sides decide alike), on masses from
+the oracle's full attention, random masses, the closed-form diagonal and
+axial cases, several tau / lambda, both token orders, and bad arguments."""
+
+import math
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_major_amd as sa
+import oracle
+from oracle import search
+
+
+def _groups(spec, heads):
+    rows = [(lo, hi, 0, 0, 0, 0) for lo, hi in spec] * heads
+    return np.array(rows, np.int32), np.full(heads, len(spec), np.int32)
+
+
+def _compare(h, grid, tile, A, spec, tau, lam):
+    heads = A.shape[0]
+    g_in, gph = _groups(spec, heads)
+    got, rec, cost = sa.sparse_attn_search_windows(h, A, g_in, gph, tau, lam)
+    counts = oracle.tile_counts(grid, tile)
+    want, wgph, wrec, wcost = search.search(grid, tile, counts, A.astype(np.float64), [spec] * heads,
+                                            tau, lam)
+    assert np.array_equal(got, want)
+    assert np.array_equal(rec, wrec) and np.array_equal(cost, wcost)
+    return got, rec, cost
+
+
+SPEC = [(0, 0), (1, 2), (3, -1)]
+
+
+@pytest.mark.parametrize("tau,lam", [(0.0, math.inf), (0.5, math.inf), (0.9, math.inf),
+                                     (0.95, 3.0), (0.99, 1.2), (1.0, math.inf)])
+def test_matches_oracle_on_full_attention_mass(tau, lam):
+    grid, tile = (5, 12, 16), (1, 4, 4)
+    N = int(np.prod(grid))
+    rng = np.random.default_rng(1)
+    q = rng.standard_normal((2, N, 16)).astype(np.float32)
+    k = rng.standard_normal((2, N, 16)).astype(np.float32)
+    A = oracle.tile_mass(grid, tile, q, k).astype(np.float32)
+    h = sa.sparse_attn_create(2, 128, grid, tile, "bf16")
+    _compare(h, grid, tile, A, SPEC, tau, lam)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_matches_oracle_on_random_masses(seed):
+    grid, tile = (4, 20, 36), (1, 8, 16)  # clipped tiles
+    nT = oracle.num_tiles(grid, tile)
+    rng = np.random.default_rng(seed)
+    A = rng.random((3, nT, nT)) ** 4
+    A = (A / A.sum(axis=2, keepdims=True)).astype(np.float32)
+    h = sa.sparse_attn_create(3, 128, grid, tile, "bf16")
+    for tau, lam in ((0.8, math.inf), (0.9, 2.0), (0.97, 1.1)):
+        _compare(h, grid, tile, A, [(0, 1), (2, -1)], tau, lam)
+
+
+def test_diagonal_and_axial_cases():
+    grid, tile = (3, 12, 16), (1, 4, 4)
+    nT = oracle.num_tiles(grid, tile)
+    h = sa.sparse_attn_create(1, 128, grid, tile, "bf16")
+    g, _, _ = _compare(h, grid, tile, np.eye(nT, dtype=np.float32)[None], SPEC, 1.0, math.inf)
+    assert np.array_equal(oracle.mask_from_windows(grid, tile, g, [3])[0], np.eye(nT, dtype=np.uint8))
+    a, b, e, _ = search._tile_coords(grid, tile)
+    same = (a[:, None] == a[None, :]) & ((b[:, None] == b[None, :]) | (e[:, None] == e[None, :]))
+    A = (same / same.sum(axis=1, keepdims=True)).astype(np.float32)
+    g, _, _ = _compare(h, grid, tile, A[None], SPEC, 1.0, math.inf)
+    assert np.array_equal(oracle.mask_from_windows(grid, tile, g, [3])[0], same.astype(np.uint8))
+
+
+def test_hilbert_order_searches_bands_along_the_curve():
+    grid, tile = (3, 20, 36), (1, 8, 16)
+    N = int(np.prod(grid))
+    g1, t1 = (1, 1, N), (1, 1, 128)
+    nT = oracle.num_tiles(g1, t1)
+    rng = np.random.default_rng(5)
+    A = rng.random((2, nT, nT)) ** 6
+    A = (A / A.sum(axis=2, keepdims=True)).astype(np.float32)
+    h = sa.sparse_attn_create(2, 128, grid, tile, "bf16", order="hilbert")
+    _compare(h, g1, t1, A, [(0, -1)], 0.9, math.inf)
+
+
+def test_argument_checks():
+    grid, tile = (3, 12, 16), (1, 4, 4)
+    nT = oracle.num_tiles(grid, tile)
+    h = sa.sparse_attn_create(1, 128, grid, tile, "bf16")
+    A = np.full((1, nT, nT), 1.0 / nT, np.float32)
+    g, gph = _groups(SPEC, 1)
+    for tau, lam in ((1.5, 1.0), (-0.1, 1.0), (0.5, 0.0), (0.5, float("nan"))):
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_search_windows(h, A, g, gph, tau, lam)
+        assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    bad = np.array([(1, 2, 0, 0, 0, 0), (0, 0, 0, 0, 0, 0)], np.int32)  # unsorted groups
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_search_windows(h, A, bad, [2], 0.5)
+    assert e.value.status == sa.SPARSE_ATTN_BAD_MASK
