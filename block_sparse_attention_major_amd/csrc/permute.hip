@@ -70,43 +70,56 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(Layout L, int vp
 }
 
 // Raster bf16 rows -> per-tile transposed block [D][B]: row f of tile tau
-// holds feature f of slots 0..B-1 (empty slots 0).  The tile passes through
-// LDS as [B][D + 2] so the transposed reads spread over banks.
+// holds feature f of slots 0..B-1 (empty slots 0).  Rows are gathered with
+// 16-byte loads into LDS words [B][D / 2 + 1] (an odd word stride, so the
+// column reads below spread over the banks); each output item then reads a
+// feature pair of 8 consecutive slots as 8 words and writes two 16-byte
+// vectors, one per feature.
 template <int D>
 __global__ __launch_bounds__(kThreads) void permute_tile_columns_kernel(
     Layout L, const uint16_t *__restrict__ src, uint16_t *__restrict__ dst)
 {
-    constexpr int LD = D + 2;
-    __shared__ uint16_t tileT[128 * LD];
+    constexpr int LDW = D / 2 + 1;  // words per LDS row
+    constexpr int CPR = D / 8;      // 16-byte chunks per row
+    __shared__ uint32_t tileW[128 * LDW];
     const int h = blockIdx.x / L.nT;
     const int tau = blockIdx.x - h * L.nT;
     const TileBox bx = tile_box(L, tau);
     const int c = bx.et * bx.ey * bx.ex;
     const int B = L.B;
-    // Gather the real rows (zero the empty ones) into LDS, 4 bytes at a time.
-    constexpr int WPR = D / 2;  // 32-bit words per row
-    for (int u = threadIdx.x; u < B * WPR; u += kThreads) {
-        const int slot = u / WPR, w = u - slot * WPR;
-        uint32_t val = 0;
-        if (slot < c) {
-            const long long n = position_token(L, slot_token(L, bx, slot));
-            val = reinterpret_cast<const uint32_t *>(src + ((long long)h * L.N + n) * D)[w];
-        }
-        tileT[slot * LD + 2 * w] = (uint16_t)(val & 0xFFFF);
-        tileT[slot * LD + 2 * w + 1] = (uint16_t)(val >> 16);
+    const uint4 *rows = reinterpret_cast<const uint4 *>(src + (long long)h * L.N * D);
+    for (int u = threadIdx.x; u < B * CPR; u += kThreads) {
+        const int slot = u / CPR, ch = u - slot * CPR;
+        uint4 val = make_uint4(0, 0, 0, 0);
+        if (slot < c)
+            val = rows[(long long)position_token(L, slot_token(L, bx, slot)) * CPR + ch];
+        uint32_t *w = tileW + slot * LDW + 4 * ch;
+        w[0] = val.x;
+        w[1] = val.y;
+        w[2] = val.z;
+        w[3] = val.w;
     }
     __syncthreads();
-    // Write row f: B slots, 8 per 16-byte vector.
-    const int vpr = B / 8;
+    const int groups = B / 8;
     uint16_t *out = dst + ((long long)h * L.nT + tau) * D * B;
-    for (int u = threadIdx.x; u < D * vpr; u += kThreads) {
-        const int f = u / vpr, g = u - f * vpr;
-        uint32_t w[4];
+    for (int u = threadIdx.x; u < (D / 2) * groups; u += kThreads) {
+        const int fp = u / groups, g = u - fp * groups;
+        uint32_t w[8];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            w[k] = (uint32_t)tileT[(8 * g + 2 * k) * LD + f] |
-                   ((uint32_t)tileT[(8 * g + 2 * k + 1) * LD + f] << 16);
-        reinterpret_cast<uint4 *>(out + (long long)f * B)[g] = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int i = 0; i < 8; ++i)
+            w[i] = tileW[(8 * g + i) * LDW + fp];
+        // Low halves are feature 2 fp, high halves feature 2 fp + 1.
+        uint4 lo, hi;
+        lo.x = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+        lo.z = __builtin_amdgcn_perm(w[5], w[4], 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(w[7], w[6], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(w[5], w[4], 0x07060302u);
+        hi.w = __builtin_amdgcn_perm(w[7], w[6], 0x07060302u);
+        reinterpret_cast<uint4 *>(out + (long long)(2 * fp) * B)[g] = lo;
+        reinterpret_cast<uint4 *>(out + (long long)(2 * fp + 1) * B)[g] = hi;
     }
 }
 
