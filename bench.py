@@ -205,6 +205,28 @@ def window_search(sa, wl, q, k, v, stream, tau=0.9):
                     "host greedy dual-window search per head, attention stage under the searched mask"}
 
 
+def gemm_reference(stream, n=16384, reps=5):
+    """A dense bf16 library GEMM (torch.matmul, n x n x n) on the same GPU:
+    what a plain matrix product sustains here under the same power and clock
+    conditions, as context for the attention kernel's fraction of the
+    published peak."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    for _ in range(2):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        c = a @ b
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": [n, n, n], "ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +236,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
     ap.add_argument("--no-search", action="store_true", help="skip the window-search measurement")
+    ap.add_argument("--no-gemm-reference", action="store_true", help="skip the library GEMM reference")
     ap.add_argument("--no-order-comparison", action="store_true",
                     help="skip the tile-box / Hilbert-order top-k comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -339,6 +362,7 @@ def main():
     select_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
     del sel_bitmap
 
+    gemm = None if args.no_gemm_reference else gemm_reference(stream)
     searched = None
     if not args.no_search:
         searched = window_search(sa, wl, q, k, v, stream)
@@ -382,7 +406,8 @@ def main():
                            "written in raster order by the attention kernels)"},
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "flops_per_launch": F},
+                     "traffic": traffic, "flops_per_launch": F,
+                     "library_gemm_reference": gemm},
         "attention": {"ms": attn_ms, "ms_min": float(attn_min), "tflops": attn_tflops,
                       "pct_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS,
                       "tflops_issued": info["flops_issued"] / (attn_ms * 1e-3) / 1e12,
