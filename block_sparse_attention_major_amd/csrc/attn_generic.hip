@@ -8,7 +8,9 @@
 // One workgroup of 256 threads per (head, query tile); two threads per query
 // slot, each owning half of the features (partial dot products are combined
 // with the neighbouring lane).  Keys pass through LDS 64 at a time and are
-// processed 16 at a time with an online softmax.
+// processed 16 at a time with an online softmax.  Q and O rows go to the
+// caller's raster tensors or the tile-major workspace, and the log-sum-exp
+// is written on request.
 #include "common.h"
 
 namespace sa {

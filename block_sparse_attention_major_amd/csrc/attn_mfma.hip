@@ -22,7 +22,8 @@
 //    transposed V tile of a stage are copied global -> LDS by the DMA path
 //    (global_load_lds_dwordx4: no registers, no LDS store instructions) into
 //    a ring of four statically addressed slots, two stages ahead of the
-//    math, the copies interleaved with the matrix products.  The empty tail
+//    math, issued at the start of the softmax phase (the other group's
+//    wave keeps the matrix core busy meanwhile).  The empty tail
 //    of a clipped key tile (80 of 128 slots at 720p) is skipped at 32-key
 //    granularity.
 //  - Workgroups follow the compiled longest-first order of the pair lists,
@@ -41,6 +42,11 @@
 //    16 distinct chunk positions per 16 lanes.
 //  - Online softmax in fp32 and exp2 with a lazily moved running max; row
 //    sums are taken from the bf16 probabilities with v_dot2.
+//  - Each lane reads its query row of Q and writes its row of O either in
+//    the caller's raster tensors (the forward: the Q permute and O
+//    unpermute are fused here, real slots only) or in the tile-major
+//    workspace; optionally it writes the query's log-sum-exp, m + log2 l
+//    scaled back to natural log, from the same running max and row sum.
 #include "common.h"
 
 namespace sa {

@@ -36,6 +36,9 @@
 //    16 distinct chunk positions per 16 lanes.
 //  - Online softmax in fp32 and exp2 with a lazily moved running max; row
 //    sums are taken from the bf16 probabilities with v_dot2.
+//  - Q and O rows go to the caller's raster tensors or the tile-major
+//    workspace, and the log-sum-exp is written on request, as in the pair
+//    kernel.
 #include "common.h"
 
 namespace sa {
