@@ -29,14 +29,7 @@ constexpr int kTileRows = 128;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Max over the 64 lanes of a wave.
-__device__ __forceinline__ float wave_max(float x)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        x = fmaxf(x, __shfl_xor(x, o));
-    return x;
-}
+// Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float x)
 {
 #pragma unroll

@@ -11,11 +11,13 @@
 //
 //   pool   : one workgroup per (head, tile, Q or K): fp32 mean of the tile's
 //            real rows of the tile-major Q or K
-//   select : one workgroup per (head, query tile): the row's nT scores into
-//            LDS as order-preserving 32-bit keys, the k-th largest key by a
-//            4-pass radix select (8 bits per pass, most significant first),
-//            then the row: keys above it, and keys equal to it in increasing
-//            j until k are kept (a workgroup-wide prefix count over j).
+//   select : one workgroup per (head, 8 query tiles; 1 when nT > 2048): the
+//            rows' nT scores into LDS as order-preserving 32-bit keys (each
+//            k-bar row read once for the group), then one wave per row: the
+//            k-th largest key by a bitwise radix select over the candidates
+//            (32 rounds of ballots, most significant bit first), and the
+//            row: keys above it, and keys equal to it in increasing j until
+//            k are kept (ballot prefix counts).
 #include "common.h"
 
 namespace sa {
@@ -94,106 +96,96 @@ __device__ __forceinline__ uint32_t sort_key(float x)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// Exclusive prefix count of `flag` over the workgroup's threads (in thread
-// order); returns the count before this thread, *total the workgroup's count.
-__device__ __forceinline__ int block_prefix_count(bool flag, int *wave_cnt, int *total)
-{
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const unsigned long long bits = __ballot(flag);
-    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-    const int in_wave = __popcll(bits & below);
-    __syncthreads();  // wave_cnt is free again
-    if (lane == 0)
-        wave_cnt[wave] = __popcll(bits);
-    __syncthreads();
-    int before = 0, all = 0;
-    for (int w = 0; w < kSelThreads / 64; ++w) {
-        before += w < wave ? wave_cnt[w] : 0;
-        all += wave_cnt[w];
-    }
-    *total = all;
-    return before + in_wave;
-}
-
-// blockIdx.x = h * nT + i.  keys: dynamic LDS of nT entries.
+// blockIdx.x = h * ceil(nT / R) + g: query tiles i = g R .. g R + R - 1 of
+// head h.  Each k-bar row is read once for the R query tiles (their q-bar
+// rows wait in LDS), so the k-bar traffic is 1 / R of one row per group.
+// keys: dynamic LDS [R][nT].
+template <int R>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(Layout L, const float *__restrict__ qbar,
                                                              const float *__restrict__ kbar,
                                                              const int *__restrict__ kh, float scale,
                                                              uint8_t *__restrict__ bitmap)
 {
     extern __shared__ uint32_t keys[];
-    __shared__ float qi[128];
-    __shared__ int hist[256];
-    __shared__ int wave_cnt[kSelThreads / 64];
-    __shared__ uint32_t sel[2];  // prefix digit found by a pass, remaining count
+    __shared__ float qi[R][128];
     const int nT = L.nT, D = L.D;
-    const int hi = blockIdx.x;
-    const int h = hi / nT;
+    const int ngroups = (nT + R - 1) / R;
+    const int h = blockIdx.x / ngroups;
+    const int i0 = (blockIdx.x - h * ngroups) * R;
+    const int rows = min(R, nT - i0);
     const int tid = threadIdx.x;
     const int kk = kh[h];
-    uint8_t *out = bitmap + (long long)hi * nT;
     if (kk <= 0 || kk >= nT) {
-        for (int j = tid; j < nT; j += kSelThreads)
-            out[j] = kk > 0 ? 1 : 0;
+        for (int u = tid; u < rows * nT; u += kSelThreads)
+            bitmap[((long long)h * nT + i0) * nT + u] = kk > 0 ? 1 : 0;
         return;
     }
-    for (int e = tid; e < D; e += kSelThreads)
-        qi[e] = qbar[(long long)hi * D + e];
+    for (int u = tid; u < R * D; u += kSelThreads) {
+        const int r = u / D, e = u - r * D;
+        qi[r][e] = r < rows ? qbar[((long long)h * nT + i0 + r) * D + e] : 0.f;
+    }
     __syncthreads();
     const float *kb = kbar + (long long)h * nT * D;
     for (int j = tid; j < nT; j += kSelThreads) {
         const float4 *kr = (const float4 *)(kb + (long long)j * D);
-        float dot = 0.f;
+        float dot[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            dot[r] = 0.f;
         for (int e4 = 0; e4 < D / 4; ++e4) {
             const float4 v = kr[e4];
-            dot = fmaf(qi[4 * e4], v.x, dot);
-            dot = fmaf(qi[4 * e4 + 1], v.y, dot);
-            dot = fmaf(qi[4 * e4 + 2], v.z, dot);
-            dot = fmaf(qi[4 * e4 + 3], v.w, dot);
-        }
-        keys[j] = sort_key(dot * scale);
-    }
-    // Radix select of the kk-th largest key.
-    uint32_t prefix = 0, pmask = 0;
-    int remaining = kk;
-    for (int pass = 3; pass >= 0; --pass) {
-        const int shift = 8 * pass;
-        for (int b = tid; b < 256; b += kSelThreads)
-            hist[b] = 0;
-        __syncthreads();
-        for (int j = tid; j < nT; j += kSelThreads) {
-            const uint32_t key = keys[j];
-            if ((key & pmask) == prefix)
-                atomicAdd(&hist[(key >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int above = 0, b = 255;
-            for (; b > 0; --b) {
-                if (above + hist[b] >= remaining)
-                    break;
-                above += hist[b];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                dot[r] = fmaf(qi[r][4 * e4], v.x, dot[r]);
+                dot[r] = fmaf(qi[r][4 * e4 + 1], v.y, dot[r]);
+                dot[r] = fmaf(qi[r][4 * e4 + 2], v.z, dot[r]);
+                dot[r] = fmaf(qi[r][4 * e4 + 3], v.w, dot[r]);
             }
-            sel[0] = (uint32_t)b;
-            sel[1] = (uint32_t)(remaining - above);
         }
-        __syncthreads();
-        prefix |= sel[0] << shift;
-        pmask |= 255u << shift;
-        remaining = (int)sel[1];
-        __syncthreads();  // sel is rewritten by the next pass
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            keys[r * nT + j] = sort_key(dot[r] * scale);
     }
-    // Keep keys above the threshold, and the first `remaining` equal ones.
-    int taken_eq = 0;
-    for (int j0 = 0; j0 < nT; j0 += kSelThreads) {
-        const int j = j0 + tid;
-        const uint32_t key = j < nT ? keys[j] : 0u;
-        const bool eq = j < nT && key == prefix;
-        int total;
-        const int rank = taken_eq + block_prefix_count(eq, wave_cnt, &total);
-        if (j < nT)
-            out[j] = (key > prefix || (eq && rank < remaining)) ? 1 : 0;
-        taken_eq += total;
+    __syncthreads();
+    // One wave per row: the k-th largest key by a bitwise radix select with
+    // ballots (candidates = keys matching the bits fixed so far), then the
+    // row.  Key j sits in lane j % 64 of slot j / 64.
+    const int lane = tid & 63, wave = tid >> 6;
+    const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int slots = (nT + 63) / 64;
+    for (int r = wave; r < rows; r += kSelThreads / 64) {
+        const uint32_t *rk = keys + r * nT;
+        uint32_t prefix = 0, fixed = 0;  // value and mask of the bits fixed so far
+        int remaining = kk;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t b = 1u << bit;
+            int ones = 0;
+            for (int sl = 0; sl < slots; ++sl) {
+                const int j = sl * 64 + lane;
+                const uint32_t key = j < nT ? rk[j] : 0u;
+                const bool cand = j < nT && (key & fixed) == prefix;
+                ones += __popcll(__ballot(cand && (key & b)));
+            }
+            if (ones >= remaining)
+                prefix |= b;
+            else
+                remaining -= ones;
+            fixed |= b;
+        }
+        // prefix is the k-th largest key; keep the keys above it and the
+        // first `remaining` keys equal to it in increasing j.
+        uint8_t *out = bitmap + ((long long)h * nT + i0 + r) * nT;
+        int taken_eq = 0;
+        for (int sl = 0; sl < slots; ++sl) {
+            const int j = sl * 64 + lane;
+            const uint32_t key = j < nT ? rk[j] : 0u;
+            const bool eq = j < nT && key == prefix;
+            const unsigned long long eqs = __ballot(eq);
+            const int rank = taken_eq + __popcll(eqs & below);
+            if (j < nT)
+                out[j] = (key > prefix || (eq && rank < remaining)) ? 1 : 0;
+            taken_eq += __popcll(eqs);
+        }
     }
 }
 
@@ -210,9 +202,16 @@ hipError_t launch_select_topk(const Layout &L, int elem_bytes, const void *q, co
     else
         hipLaunchKernelGGL(pool_kernel<float>, pool_grid, dim3(kPoolThreads), 0, s, L, (const float *)q,
                            (const float *)k, qbar, kbar);
-    const size_t lds = sizeof(uint32_t) * (size_t)L.nT;
-    hipLaunchKernelGGL(select_kernel, dim3(L.heads * L.nT), dim3(kSelThreads), lds, s, L, qbar, kbar, kh,
-                       scale, bitmap);
+    // R query tiles per workgroup, their keys in LDS (at most 64 KB).
+    constexpr int R = 8;
+    if ((size_t)R * L.nT * sizeof(uint32_t) <= 65536) {
+        const dim3 grid(L.heads * ((L.nT + R - 1) / R));
+        hipLaunchKernelGGL(select_kernel<R>, grid, dim3(kSelThreads), sizeof(uint32_t) * (size_t)R * L.nT, s, L,
+                           qbar, kbar, kh, scale, bitmap);
+    } else {
+        hipLaunchKernelGGL(select_kernel<1>, dim3(L.heads * L.nT), dim3(kSelThreads),
+                           sizeof(uint32_t) * (size_t)L.nT, s, L, qbar, kbar, kh, scale, bitmap);
+    }
     return hipGetLastError();
 }
 
