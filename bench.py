@@ -323,6 +323,21 @@ def main():
     torch.cuda.synchronize()
     attn_lse_ms = float(np.mean([a.elapsed_time(b) for a, b in lse_ev]))
     del lse
+
+    # The standalone unpermute of the three-stage path (the step fuses it
+    # into the attention epilogue).
+    sa.sparse_attn_permute_inputs(h, q, k, v, ws)
+    sa.sparse_attn_attend(h, ws)
+    sa.sparse_attn_unpermute_output(h, ws, o)
+    unp = []
+    for _ in range(5):
+        a, b = E(), E()
+        a.record(stream)
+        sa.sparse_attn_unpermute_output(h, ws, o)
+        b.record(stream)
+        unp.append((a, b))
+    torch.cuda.synchronize()
+    unperm_ms = float(np.mean([a.elapsed_time(b) for a, b in unp]))
     nnz, overflow = sa.sparse_attn_mask_info(h)
     assert nnz == info["nnz"] and not overflow, (nnz, info["nnz"], overflow)
 
@@ -420,7 +435,14 @@ def main():
                       "dense_tflops": info["flops_dense"] / (dense_ms * 1e-3) / 1e12 if dense_ms else None,
                       "with_lse_ms": attn_lse_ms},
         "stages_ms": {"mask_compile": mask_ms, "permute_kv": perm_ms, "attention": attn_ms},
-        "stages_gbs": {"permute_kv": perm_bytes / (perm_ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS},
+        "stages_gbs": {"permute_kv": perm_bytes / (perm_ms * 1e-3) / 1e9,
+                       "unpermute_o_standalone": 2 * in_bytes / (unperm_ms * 1e-3) / 1e9,
+                       "mask_compile": mask_buf.numel() / (mask_ms * 1e-3) / 1e9,
+                       "peak": PEAK_HBM_GBS,
+                       "note": "unpermute: real rows read + written, timed outside the step (the step "
+                               "fuses it); mask compile: bytes of the compiled-mask buffer per call, "
+                               "a launch- and latency-bound integer stage"},
+        "unpermute_o_standalone_ms": unperm_ms,
         "tile_selection": {"ms": select_ms, "k_per_head": [int(x) for x in kh],
                            "pool_gbs": 2 * in_bytes / (select_ms * 1e-3) / 1e9,
                            "note": "top-k over mean-pooled tile scores from the permuted Q, K; "
