@@ -199,6 +199,8 @@ struct MaskBuffers {
     int nchunks;
     int pair;       // 0: rows r = h nT + i; 1: pairs r = h nP + pr (entries carry keep bits)
     int *flag;      // pairs only, [R]: 1 = the pair kernel serves the pair (see kPairNum)
+    FastDiv dplane; // ny * nx: tiles per tile-grid plane
+    FastDiv drow;   // nx: tiles per tile-grid row
 };
 
 // A pair of query tiles goes to the pair kernel when the union of their key

@@ -42,12 +42,20 @@ struct RowCtx {
     int g0, g1;      // group range of the head
 };
 
+// Tile coordinates (a, b, e) of tile j, by multiply-high division.
+__device__ __forceinline__ void tile_coords(const Layout &L, const MaskBuffers &mb, int j, int &a, int &b,
+                                            int &e)
+{
+    a = (int)fast_div((uint32_t)j, mb.dplane);
+    const int rem = j - a * L.ny * L.nx;
+    b = (int)fast_div((uint32_t)rem, mb.drow);
+    e = rem - b * L.nx;
+}
+
 __device__ __forceinline__ RowCtx tile_ctx(const Layout &L, const MaskBuffers &mb, int h, int i)
 {
     RowCtx c;
-    c.ai = i / (L.ny * L.nx);
-    c.bi = (i / L.nx) % L.ny;
-    c.ei = i % L.nx;
+    tile_coords(L, mb, i, c.ai, c.bi, c.ei);
     c.g0 = mb.group_off[h];
     c.g1 = mb.group_off[h + 1];
     return c;
@@ -56,7 +64,8 @@ __device__ __forceinline__ RowCtx tile_ctx(const Layout &L, const MaskBuffers &m
 __device__ __forceinline__ bool window_keeps(const Layout &L, const MaskBuffers &mb,
                                              const RowCtx &c, int j)
 {
-    const int aj = j / (L.ny * L.nx), bj = (j / L.nx) % L.ny, ej = j % L.nx;
+    int aj, bj, ej;
+    tile_coords(L, mb, j, aj, bj, ej);
     const int dt = abs(c.ai - aj), dy = abs(c.bi - bj), dx = abs(c.ei - ej);
     for (int g = c.g0; g < c.g1; ++g) {
         const int *G = mb.groups + 6 * g;  // dt_lo, dt_hi, ry0, ry1, rx0, rx1
@@ -204,8 +213,11 @@ __global__ __launch_bounds__(1024) void scan_kernel(Layout L, MaskBuffers mb)
     }
     // Rows per length, then bucket starts in decreasing length order.
     const int nL = L.nT + 1;
+    // (Threads take consecutive lengths, so each chunk row is read
+    // coalesced; the loop is unrolled so several reads are in flight.)
     for (int len = threadIdx.x; len < nL; len += blockDim.x) {
         int tot = 0;
+#pragma unroll 8
         for (int c = 0; c < mb.nchunks; ++c)
             tot += mb.chunk[(long long)c * nL + len];
         mb.bucket[len] = tot;
@@ -217,13 +229,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(Layout L, MaskBuffers mb)
     __syncthreads();
     // Base of each (chunk, length): bucket start + rows of that length in
     // earlier chunks.
+    constexpr int kBatch = 8;
     for (int len = threadIdx.x; len < nL; len += blockDim.x) {
         int run = mb.bucket[len];
-        for (int c = 0; c < mb.nchunks; ++c) {
-            int *p = &mb.chunk[(long long)c * nL + len];
-            const int x = *p;
-            *p = run;
-            run += x;
+        for (int c0 = 0; c0 < mb.nchunks; c0 += kBatch) {
+            int x[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                x[u] = c0 + u < mb.nchunks ? mb.chunk[(long long)(c0 + u) * nL + len] : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (c0 + u < mb.nchunks)
+                    mb.chunk[(long long)(c0 + u) * nL + len] = run;
+                run += x[u];
+            }
         }
     }
 }

@@ -538,6 +538,8 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
     mb.nchunks = ml.nchunks;
     mb.pair = 0;
     mb.flag = nullptr;
+    mb.dplane = sa::make_fastdiv(uint32_t(L.ny) * uint32_t(L.nx));
+    mb.drow = sa::make_fastdiv(uint32_t(L.nx));
     sa::MaskBuffers pb{};
     if (pairs) {
         pb = mb;
