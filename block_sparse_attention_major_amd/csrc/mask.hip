@@ -39,7 +39,13 @@ constexpr int kWave = 64;
 
 struct RowCtx {
     int ai, bi, ei;  // query tile coordinates
-    int g0, g1;      // group range of the head
+};
+
+// The window groups of one head, read once per list into registers:
+// rows of (dt_lo, dt_hi, ry0, ry1, rx0, rx1).
+struct Windows {
+    int n;
+    int g[SPARSE_ATTN_MAX_GROUPS][6];
 };
 
 // Tile coordinates (a, b, e) of tile j, by multiply-high division.
@@ -52,50 +58,40 @@ __device__ __forceinline__ void tile_coords(const Layout &L, const MaskBuffers &
     e = rem - b * L.nx;
 }
 
-__device__ __forceinline__ RowCtx tile_ctx(const Layout &L, const MaskBuffers &mb, int h, int i)
+__device__ __forceinline__ RowCtx tile_ctx(const Layout &L, const MaskBuffers &mb, int i)
 {
     RowCtx c;
     tile_coords(L, mb, i, c.ai, c.bi, c.ei);
-    c.g0 = mb.group_off[h];
-    c.g1 = mb.group_off[h + 1];
     return c;
 }
 
-__device__ __forceinline__ bool window_keeps(const Layout &L, const MaskBuffers &mb,
-                                             const RowCtx &c, int j)
+__device__ __forceinline__ bool window_keeps(const RowCtx &c, const Windows &w, int aj, int bj, int ej)
 {
-    int aj, bj, ej;
-    tile_coords(L, mb, j, aj, bj, ej);
     const int dt = abs(c.ai - aj), dy = abs(c.bi - bj), dx = abs(c.ei - ej);
-    for (int g = c.g0; g < c.g1; ++g) {
-        const int *G = mb.groups + 6 * g;  // dt_lo, dt_hi, ry0, ry1, rx0, rx1
-        if (dt < G[0] || (G[1] >= 0 && dt > G[1]))
-            continue;
-        if (G[2] >= 0 && G[4] >= 0 && dy <= G[2] && dx <= G[4])
-            return true;
-        if (G[3] >= 0 && G[5] >= 0 && dy <= G[3] && dx <= G[5])
-            return true;
+#pragma unroll
+    for (int g = 0; g < SPARSE_ATTN_MAX_GROUPS; ++g) {
+        if (g < w.n) {
+            const int *G = w.g[g];
+            if (dt < G[0] || (G[1] >= 0 && dt > G[1]))
+                continue;
+            if (G[2] >= 0 && G[4] >= 0 && dy <= G[2] && dx <= G[4])
+                return true;
+            if (G[3] >= 0 && G[5] >= 0 && dy <= G[3] && dx <= G[5])
+                return true;
+        }
     }
     return false;
 }
 
-template <int KIND>
-__device__ __forceinline__ bool keeps(const Layout &L, const MaskBuffers &mb,
-                                      const uint8_t *__restrict__ bitmap, const RowCtx &c, int h,
-                                      int i, int j)
-{
-    if (KIND == 0)
-        return bitmap[((long long)h * L.nT + i) * L.nT + j] != 0;
-    return window_keeps(L, mb, c, j);
-}
-
 // The query tiles behind list r: one tile for a row list, two (t2 = -1: one)
-// for a pair list.
+// for a pair list, and (window masks) the head's groups.
 struct ListRow {
     int h, t1, t2;
     RowCtx c1, c2;
+    Windows w;
 };
 
+template <int KIND>
 __device__ __forceinline__ ListRow list_row(const Layout &L, const MaskBuffers &mb, int r)
 {
     ListRow q;
@@ -109,8 +105,18 @@ __device__ __forceinline__ ListRow list_row(const Layout &L, const MaskBuffers &
         q.t1 = r - q.h * L.nT;
         q.t2 = -1;
     }
-    q.c1 = tile_ctx(L, mb, q.h, q.t1);
-    q.c2 = tile_ctx(L, mb, q.h, q.t2 >= 0 ? q.t2 : q.t1);
+    q.c1 = tile_ctx(L, mb, q.t1);
+    q.c2 = tile_ctx(L, mb, q.t2 >= 0 ? q.t2 : q.t1);
+    q.w.n = 0;
+    if (KIND == 1) {
+        const int g0 = mb.group_off[q.h];
+        q.w.n = mb.group_off[q.h + 1] - g0;
+#pragma unroll
+        for (int g = 0; g < SPARSE_ATTN_MAX_GROUPS; ++g)
+#pragma unroll
+            for (int k = 0; k < 6; ++k)
+                q.w.g[g][k] = g < q.w.n ? mb.groups[6 * (g0 + g) + k] : 0;
+    }
     return q;
 }
 
@@ -120,8 +126,17 @@ template <int KIND>
 __device__ __forceinline__ int keep_bits(const Layout &L, const MaskBuffers &mb,
                                          const uint8_t *__restrict__ bitmap, const ListRow &q, int j)
 {
-    int bits = keeps<KIND>(L, mb, bitmap, q.c1, q.h, q.t1, j) ? 1 : 0;
-    if (q.t2 >= 0 && keeps<KIND>(L, mb, bitmap, q.c2, q.h, q.t2, j))
+    if (KIND == 0) {
+        const uint8_t *row = bitmap + (long long)q.h * L.nT * L.nT;
+        int bits = row[(long long)q.t1 * L.nT + j] != 0 ? 1 : 0;
+        if (q.t2 >= 0 && row[(long long)q.t2 * L.nT + j] != 0)
+            bits |= 2;
+        return bits;
+    }
+    int aj, bj, ej;
+    tile_coords(L, mb, j, aj, bj, ej);
+    int bits = window_keeps(q.c1, q.w, aj, bj, ej) ? 1 : 0;
+    if (q.t2 >= 0 && window_keeps(q.c2, q.w, aj, bj, ej))
         bits |= 2;
     return bits;
 }
@@ -141,7 +156,7 @@ __global__ __launch_bounds__(256) void count_kernel(Layout L, MaskBuffers mb,
     if (r >= mb.R)
         return;
     const int lane = threadIdx.x & 63;
-    const ListRow q = list_row(L, mb, r);
+    const ListRow q = list_row<KIND>(L, mb, r);
     // n: list length (union for a pair); n12: kept entries of each tile
     // summed (a pair's two row lengths).
     int n = 0, n12 = 0;
@@ -257,7 +272,7 @@ __global__ __launch_bounds__(256) void fill_kernel(Layout L, MaskBuffers mb,
     if (mb.pair && !mb.flag[r])
         return;  // no list: the row kernel serves both tiles
     const int lane = threadIdx.x & 63;
-    const ListRow q = list_row(L, mb, r);
+    const ListRow q = list_row<KIND>(L, mb, r);
     const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     long long base = mb.row_ptr[r];
     for (int j0 = 0; j0 < L.nT; j0 += kWave) {
