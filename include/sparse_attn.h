@@ -34,6 +34,8 @@
  *     behind.  sparse_attn_last_error() then describes the failure.
  *   - Device pointers are caller-owned HIP device memory (for example torch
  *     tensors), 16-byte aligned.  The library never allocates device memory.
+ *   - Host arrays a call takes (window specs, per-head k) are read or
+ *     staged before the call returns; the caller may reuse them at once.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *     work and return without synchronizing, unless stated otherwise.
  *     Asynchronous faults surface at the caller's next synchronization.
