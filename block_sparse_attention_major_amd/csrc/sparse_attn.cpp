@@ -30,6 +30,8 @@ struct sparse_attn_handle {
     // source of sparse_attn_set_order's upload)
     std::vector<int32_t> seq;
     bool has_order = false;
+    // host copy of the last per-head k of the tile selection (upload source)
+    std::vector<int32_t> kh;
     std::string err;
 };
 
@@ -818,7 +820,8 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
     float *kbar = reinterpret_cast<float *>(b + w.o + means);
     int *kh = reinterpret_cast<int *>(b + w.o + 2 * means);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = hipMemcpyAsync(kh, k_per_head, 4 * size_t(L.heads), hipMemcpyHostToDevice, s);
+    h->kh.assign(k_per_head, k_per_head + L.heads);
+    hipError_t e = hipMemcpyAsync(kh, h->kh.data(), 4 * size_t(L.heads), hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
         e = sa::launch_select_topk(L, h->elem_bytes, b + w.q, b + w.k, kh, h->scale, qbar, kbar, bitmap,
                                    s);
