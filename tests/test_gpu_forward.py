@@ -278,3 +278,24 @@ def test_full_size_workloads_sampled(name):
     g = as_f64(got.reshape(-1, wl.head_dim)[rows])
     assert_close(g, want, "bf16", f"{name} ({len(rows)} sampled rows)")
     assert np.all(np.isfinite(as_f64(got[:, ::997])))
+
+
+def test_forward_on_a_side_stream():
+    """Every stage is enqueued on the stream it is given: a forward on a
+    separate (default-priority) stream gives the default stream's output."""
+    wl = make_workload("small", heads=2)
+    c = Case.of(wl)
+    want, _ = gpu_forward(c)
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+        q, k, v = dev(c.q), dev(c.k), dev(c.v)
+        o = torch.zeros_like(q)
+        ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    side.synchronize()
+    torch.cuda.synchronize()
+    sa.sparse_attn_set_mask(h, mb, groups=c.groups, groups_per_head=c.gph, stream=side)
+    sa.sparse_attn_forward(h, q, k, v, o, ws, stream=side)
+    side.synchronize()
+    assert np.array_equal(host(o, c.q), want)

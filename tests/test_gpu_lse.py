@@ -193,3 +193,19 @@ def test_lse_argument_checks():
         sa.sparse_attn_attend_raster(h, q, o, ws, lse=buf[1:1 + c.heads * c.N])
     assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_token_grid(dtype):
+    """One token, one tile: the softmax has one key, so O = V exactly and
+    LSE = s q . k (the degenerate end of the method)."""
+    d = 64
+    q, k, v = (_rand((1, 1, d), s, dtype) for s in (51, 52, 53))
+    c = Inputs((1, 1, 1), (1, 1, 1), q, k, v, dtype, np.ones((1, 1, 1), np.uint8))
+    o, lse = _gpu(c, "forward_lse")
+    assert np.array_equal(o, v)
+    want = float(as_f64(q)[0, 0] @ as_f64(k)[0, 0]) / np.sqrt(d)
+    assert abs(float(lse[0, 0]) - want) <= 1e-5 * max(1.0, abs(want))
+    c.M = np.zeros((1, 1, 1), np.uint8)
+    o, lse = _gpu(c, "forward_lse")
+    assert np.all(as_f64(o) == 0.0) and np.isneginf(lse[0, 0])
