@@ -20,10 +20,14 @@
 //    while the other runs its exponentials (schedule in the kernel body).
 //  - Keys are consumed in stages of 64 (half a key tile).  K and the
 //    transposed V tile of a stage are copied global -> LDS by the DMA path
-//    (global_load_lds_dwordx4: no registers, no LDS store instructions) into
-//    a ring of four statically addressed slots, two stages ahead of the
-//    math, issued at the start of the softmax phase (the other group's
-//    wave keeps the matrix core busy meanwhile).  The empty tail
+//    (buffer_load_dwordx4 ... lds: no registers, no LDS store instructions)
+//    into a ring of four statically addressed slots, two stages ahead of
+//    the math, issued at the start of the softmax phase (the other group's
+//    wave keeps the matrix core busy meanwhile).  The buffer form, unlike
+//    the global one, lets the compiler count the LDS operand reads
+//    precisely while copies are in flight (with a global-to-LDS copy
+//    pending it waits for every outstanding LDS read at each use, which
+//    defeats the read-ahead).  The empty tail
 //    of a clipped key tile (80 of 128 slots at 720p) is skipped at 32-key
 //    granularity.
 //  - Workgroups follow the compiled longest-first order of the pair lists,
@@ -37,7 +41,8 @@
 //    one query per lane (the rescale is in-lane).
 //  - V arrives pre-transposed per tile ([D][128], written by the permute
 //    stage), so V^T operand reads are plain 16-byte LDS reads, issued one
-//    k-step ahead of the products that use them.
+//    key step ahead of the products that use them (K operand reads two
+//    k-steps ahead).
 //  - LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
 //    16 distinct chunk positions per 16 lanes.
 //  - Online softmax in fp32 and exp2 with a lazily moved running max; row
@@ -140,9 +145,9 @@ struct Stage {
 // that the swizzle puts there.
 template <int D>
 struct DmaPlan {
-    const char *base;            // K of head h, or V^T of head h
-    bool is_v;                   // wave-uniform
-    int off[Stage<D>::BPW];      // byte offset of the lane's chunk within a stage
+    __amdgpu_buffer_rsrc_t rsrc;  // K of head h, or V^T of head h (N_pad D 2 bytes)
+    bool is_v;                    // wave-uniform
+    int off[Stage<D>::BPW];       // byte offset of the lane's chunk within a stage
 };
 
 template <int D>
@@ -151,8 +156,13 @@ __device__ __forceinline__ void make_plan(DmaPlan<D> &pl, const uint16_t *Kp, co
 {
     constexpr int RCK = Stage<D>::RCK, KBLK = Stage<D>::KBLK, BPW = Stage<D>::BPW;
     pl.is_v = wave * BPW >= KBLK;
-    pl.base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
-                      : (const char *)(Kp + (long long)h * L.Npad * D);
+    const char *base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
+                               : (const char *)(Kp + (long long)h * L.Npad * D);
+    // Raw buffer over one head's K (or V^T): N_pad D 2 bytes, below 2^31
+    // because the plan keeps heads * tiles^2 below 2^31.  Reads past it
+    // would return zeros instead of faulting.  Word 3 is the gfx9 raw
+    // 32-bit data format.
+    pl.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, L.Npad * D * 2, 0x00020000);
     const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
@@ -171,22 +181,22 @@ __device__ __forceinline__ void make_plan(DmaPlan<D> &pl, const uint16_t *Kp, co
     }
 }
 
-// Byte offset of stage (key tile j, half `half`) from the plan's base.
+// Byte offset of stage (key tile j, half `half`) within the head's buffer.
 template <int D>
-__device__ __forceinline__ long long stage_offset(const DmaPlan<D> &pl, int j, int half)
+__device__ __forceinline__ int stage_offset(const DmaPlan<D> &pl, int j, int half)
 {
-    return pl.is_v ? ((long long)j * D * kTile + half * kStage) * 2
-                   : ((long long)j * kTile + half * kStage) * D * 2;
+    return pl.is_v ? (j * D * kTile + half * kStage) * 2 : (j * kTile + half * kStage) * D * 2;
 }
 
 // Issue this wave's DMA block t of a stage whose K goes to Kd and V^T to Vd.
 template <int D>
-__device__ __forceinline__ void issue_block(const DmaPlan<D> &pl, char *Kd, char *Vd, const char *src,
-                                            int wave, int t)
+__device__ __forceinline__ void issue_block(const DmaPlan<D> &pl, char *Kd, char *Vd, int soff, int wave,
+                                            int t)
 {
     const int blk = wave * Stage<D>::BPW + t;
     lds_char *dst = pl.is_v ? (lds_char *)Vd + (blk - Stage<D>::KBLK) * 1024 : (lds_char *)Kd + blk * 1024;
-    __builtin_amdgcn_global_load_lds((const void *)(src + pl.off[t]), dst, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(pl.rsrc, (__attribute__((address_space(3))) void *)dst, 16,
+                                             pl.off[t], soff, 0, 0);
 }
 
 // The per-wave state of one query block: 32 queries x D features.
@@ -229,63 +239,66 @@ __device__ __forceinline__ void qk_stage(Scores &S, const char *Ks, const bf16x8
         S.s0[jj] = 0.f;
         S.s1[jj] = 0.f;
     }
-    // Operands are read one k-step ahead of the products that use them, so
-    // the LDS latency hides behind two matrix instructions.
+    // Operands are read two k-steps ahead of the products that use them, so
+    // the LDS latency hides behind four matrix instructions.
     if (two) {
-        bf16x8 a0 = *(const bf16x8 *)(Ks + kofs[0]);
-        bf16x8 a1 = *(const bf16x8 *)(Ks + SUB1 + kofs[0]);
+        bf16x8 r0[KS], r1[KS];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            r0[ks] = *(const bf16x8 *)(Ks + kofs[ks]);
+            r1[ks] = *(const bf16x8 *)(Ks + SUB1 + kofs[ks]);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 n0, n1;
-            if (ks + 1 < KS) {
-                n0 = *(const bf16x8 *)(Ks + kofs[ks + 1]);
-                n1 = *(const bf16x8 *)(Ks + SUB1 + kofs[ks + 1]);
+            if (ks + 2 < KS) {
+                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs[ks + 2]);
+                r1[ks + 2] = *(const bf16x8 *)(Ks + SUB1 + kofs[ks + 2]);
             }
-            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
-            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], S.s1, 0, 0, 0);
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
+            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[ks], qf[ks], S.s1, 0, 0, 0);
             if (ks % PER == PER - 1)
                 dma(ks / PER);
-            if (ks + 1 < KS) {
-                a0 = n0;
-                a1 = n1;
-            }
         }
-        // Keep that order: reads of step ks + 1, then the products of ks.
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        // Keep that order: reads of steps 0 and 1, then per step the reads
+        // of step ks + 2 and the products of ks.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS)
+            if (ks + 2 < KS)
                 __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
         }
     } else {
-        bf16x8 a0 = *(const bf16x8 *)(Ks + kofs[0]);
+        bf16x8 r0[KS];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            r0[ks] = *(const bf16x8 *)(Ks + kofs[ks]);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 n0;
-            if (ks + 1 < KS)
-                n0 = *(const bf16x8 *)(Ks + kofs[ks + 1]);
-            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
+            if (ks + 2 < KS)
+                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs[ks + 2]);
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
             if (ks % PER == PER - 1)
                 dma(ks / PER);
-            if (ks + 1 < KS)
-                a0 = n0;
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS)
+            if (ks + 2 < KS)
                 __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         }
     }
     if (kv < kStage) {
+        // Key 16 (jj / 8) + 8 hi + jj % 8 of each half is past the end when
+        // 16 (jj / 8) + jj % 8 >= kv - 8 hi (one register, constants inline).
+        const int lim = kv - 8 * hi;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-            const int key = 16 * (jj >> 3) + 8 * hi + (jj & 7);
-            if (key >= kv)
+            const int c = 16 * (jj >> 3) + (jj & 7);
+            if (c >= lim)
                 S.s0[jj] = -INFINITY;
-            if (32 + key >= kv)
+            if (32 + c >= lim)
                 S.s1[jj] = -INFINITY;
         }
     }
@@ -540,19 +553,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     if (beg + 1 < end)
         e_next = read_entry(beg + 1);
     // Takes the next stage: returns its descriptor (kv | bits << 8 | 1 << 10;
-    // 0 past the end) and the source of this wave's part of it.  Past the end
-    // the source is the head's first stage, always in bounds; that copy lands
-    // in a slot nobody reads again.
-    auto take = [&](const char *&src) -> int {
+    // 0 past the end) and its byte offset in this wave's buffer (K or V^T of
+    // the head).  Past the end the offset is that of the head's first stage,
+    // always in bounds; that copy lands in a slot nobody reads again.
+    auto take = [&](int &src) -> int {
         if (idx >= end) {
-            src = plan.base;
+            src = 0;
             return 0;
         }
         const int j = e_cur & 0xffff;
         const int c = (e_cur >> kPairCountShift) & 255;
         const int bits = (e_cur >> kPairBitsShift) & 3;
         const int kv = min(kStage, c - half * kStage);
-        src = plan.base + stage_offset<D>(plan, j, half);
+        src = stage_offset<D>(plan, j, half);
         const int desc = kv | (bits << 8) | (1 << 10);
         if (half == 0 && c > kStage) {
             half = 1;
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     // Descriptors: kv | bits << 8 | 1 << 10 (0: no such stage).
     int d0, d1;
     {
-        const char *src;
+        int src;
         d0 = take(src);
 #pragma unroll
         for (int t = 0; t < BPW; ++t)
@@ -636,7 +649,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         if (attends(dcur))
             qk_stage<D>(S, Kc, qf, kofs, dcur & 255, hi, [](int) {});
         lds_barrier();
-        const char *src;
+        int src;
         dnext = take(src);
 #pragma unroll
         for (int t = 0; t < BPW; ++t)

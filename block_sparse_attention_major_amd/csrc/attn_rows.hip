@@ -20,8 +20,10 @@
 //    share key tiles.
 //  - Keys are consumed in stages of 64 (half a tile).  K and the transposed V
 //    tile of a stage are copied global -> LDS by the DMA path
-//    (global_load_lds_dwordx4: no registers, no LDS store instructions) into
-//    one of two statically addressed buffers, one stage ahead of the math.
+//    (buffer_load_dwordx4 ... lds: no registers, no LDS store instructions;
+//    the buffer form keeps the compiler's LDS waits precise while copies are
+//    in flight) into one of two statically addressed buffers, one stage
+//    ahead of the math.
 //    The empty tail of a clipped key tile (80 of 128 slots at 720p) is
 //    skipped at 32-key granularity.
 //  - Scores are computed transposed, S^T = K Q^T, so each lane holds 16 keys
@@ -127,9 +129,15 @@ __device__ __forceinline__ void issue_stage(lds_char *stage, const uint16_t *__r
     constexpr int RCK = D / 8;                   // 16-byte chunks per K row
     constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
     constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
-    // Uniform bases of the stage in the permuted K and transposed V.
-    const char *kbase = (const char *)(Kp + ((long long)h * L.Npad + (long long)j * kTile + half * kStage) * D);
-    const char *vbase = (const char *)(Vt + ((long long)h * L.nT + j) * D * kTile + half * kStage);
+    // Raw buffers over head h's permuted K and transposed V (N_pad D 2
+    // bytes each, below 2^31 because the plan keeps heads * tiles^2 below
+    // 2^31); the stage is a uniform offset into them.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Kp + (long long)h * L.Npad * D), 0, L.Npad * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Vt + (long long)h * L.nT * D * kTile), 0, L.Npad * D * 2, 0x00020000);
+    const int koff = (j * kTile + half * kStage) * D * 2;
+    const int voff = (j * D * kTile + half * kStage) * 2;
     const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
@@ -137,18 +145,15 @@ __device__ __forceinline__ void issue_stage(lds_char *stage, const uint16_t *__r
         const int kb = blk < KBLK ? blk : blk - KBLK;
         const int line = 4 * kb + line_in_blk;
         const int logical = phys ^ (line & 15);
-        const char *src;
+        auto *dst = (void __attribute__((address_space(3))) *)(stage + blk * 1024);
         if (blk < KBLK) {
             constexpr int RPL = 16 / RCK;
             const int row = RPL * line + logical / RCK, c = logical % RCK;
-            src = kbase + (row * D * 2 + 16 * c);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst, 16, row * D * 2 + 16 * c, koff, 0, 0);
         } else {
             const int dv = 2 * line + (logical >> 3), c = logical & 7;
-            src = vbase + (dv * kTile * 2 + 16 * c);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, dv * kTile * 2 + 16 * c, voff, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds((const void *)src,
-                                         (void __attribute__((address_space(3))) *)(stage + blk * 1024),
-                                         16, 0, 0);
     }
 }
 
@@ -190,12 +195,15 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
                 *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi)), qf[ks], s0, 0, 0, 0);
     }
     if (kv < kStage) {
+        // Key 16 (jj / 8) + 8 hi + jj % 8 of each half is past the end when
+        // 16 (jj / 8) + jj % 8 >= kv - 8 hi (one register, constants inline).
+        const int lim = kv - 8 * hi;
 #pragma unroll
         for (int jj = 0; jj < 16; ++jj) {
-            const int key = 16 * (jj >> 3) + 8 * hi + (jj & 7);
-            if (key >= kv)
+            const int c = 16 * (jj >> 3) + (jj & 7);
+            if (c >= lim)
                 s0[jj] = -INFINITY;
-            if (32 + key >= kv)
+            if (32 + c >= lim)
                 s1[jj] = -INFINITY;
         }
     }
