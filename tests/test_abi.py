@@ -99,6 +99,21 @@ def test_create_rejects(sa, kw, code):
     assert sa.sparse_attn_last_error(None)
 
 
+def test_largest_tile_count(sa):
+    """heads * tiles^2 must stay below 2^31 (32-bit index lists, tile ids
+    below 2^16): 46,340 tiles of one head are accepted, 46,341 are not."""
+    h = sa.sparse_attn_create(1, 128, (331, 80, 224), (1, 8, 16), "bf16")
+    L = sa.sparse_attn_layout(h)
+    assert L["tiles"] == 46340 and L["tokens"] == 5931520 and L["slots"] == 5931520
+    assert 46340 ** 2 < 2 ** 31 <= 46341 ** 2
+    sa.sparse_attn_destroy(h)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_create(1, 128, (1, 24, 16 * 15447), (1, 8, 16), "bf16")  # 3 x 15,447 tiles
+    assert e.value.status == sa.SPARSE_ATTN_UNSUPPORTED
+    with pytest.raises(sa.SparseAttnError):
+        sa.sparse_attn_create(2, 128, (331, 80, 224), (1, 8, 16), "bf16")  # 2 heads of 46,340
+
+
 FAKE = 1 << 40  # aligned, never dereferenced
 
 
