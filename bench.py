@@ -309,6 +309,7 @@ def main():
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events])  # ms
     mask_ms, perm_ms, attn_ms = st.mean(axis=0)
     attn_min = st[:, 2].min()
+    attn_median = float(np.median(st[:, 2]))
 
     # The same attention launches also writing the per-query log-sum-exp.
     lse = torch.empty((wl.heads, cfg.tokens), dtype=torch.float32, device="cuda")
@@ -423,7 +424,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F,
                      "library_gemm_reference": gemm},
-        "attention": {"ms": attn_ms, "ms_min": float(attn_min), "tflops": attn_tflops,
+        "attention": {"ms": attn_ms, "ms_median": attn_median, "ms_min": float(attn_min),
+                      "tflops": attn_tflops,
                       "pct_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS,
                       # as if every kept tile pair were a full B x B block (the kernels
                       # skip padding at 32-key / 32-query granularity; the MFMA counters
@@ -449,6 +451,7 @@ def main():
                                    "not part of the timed step"},
         "topk_by_token_order": orders,
         "window_search": searched,
+        "env": env_info(),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -457,6 +460,16 @@ def main():
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
+
+
+def env_info():
+    """Device and software the numbers were taken on."""
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    return {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "memory_gb": round(props.total_memory / 2 ** 30, 1),
+            "hip": torch.version.hip, "torch": torch.__version__}
 
 
 if __name__ == "__main__":
