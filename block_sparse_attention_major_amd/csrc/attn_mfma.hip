@@ -159,9 +159,9 @@ __device__ __forceinline__ void make_plan(DmaPlan<D> &pl, const uint16_t *Kp, co
     const char *base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
                                : (const char *)(Kp + (long long)h * L.Npad * D);
     // Raw buffer over one head's K (or V^T): N_pad D 2 bytes, below 2^31
-    // because the plan keeps heads * tiles^2 below 2^31.  Reads past it
-    // would return zeros instead of faulting.  Word 3 is the gfx9 raw
-    // 32-bit data format.
+    // because the plan keeps heads * tiles^2 below 2^31, so the stage's
+    // byte offset (scalar) and the lane's offset in it (vector) both fit 32
+    // bits.  Word 3 is the gfx9 raw 32-bit data format.
     pl.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, L.Npad * D * 2, 0x00020000);
     const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
