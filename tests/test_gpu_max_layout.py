@@ -67,7 +67,7 @@ def test_largest_layout_sampled():
     # Query tiles pair along y (5 pairs per column): pairs of frames below
     # 300 run on the pair kernel, the rest on the row kernel.
     assert L["pair_axis"] == 1 and L["pair_grid"] == [NT, NY // 2, NX]
-    P = L["pairs"]
+    P = L["pairs"]  # pair rows of the one head
     i32 = dict(dtype=torch.int32, device="cuda")
     rp, cols, order, flag = (torch.empty(P + 1, **i32), torch.empty(nnz, **i32),
                              torch.empty(P, **i32), torch.empty(P, **i32))
