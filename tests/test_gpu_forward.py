@@ -299,3 +299,25 @@ def test_forward_on_a_side_stream():
     sa.sparse_attn_forward(h, q, k, v, o, ws, stream=side)
     side.synchronize()
     assert np.array_equal(host(o, c.q), want)
+
+
+def test_convenience_wrapper_matches_the_functional_calls():
+    """SparseAttention (one handle, its own mask buffer and workspace) gives
+    the functional path's output bit for bit, for a window mask and then for
+    a bitmap that needs a larger mask buffer."""
+    wl = make_workload("small", heads=2)
+    c = Case.of(wl)
+    want, _ = gpu_forward(c)
+    att = sa.SparseAttention(c.heads, c.d, c.grid, c.tile, c.dtype)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    att.set_mask_windows(c.groups, c.gph, max_nnz=int(c.mask().sum()))
+    got = att.forward(q, k, v)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got, c.q), want)
+    ones = ones_bitmap(wl)
+    att.set_mask_bitmap(dev(ones))
+    got = att.forward(q, k, v)
+    torch.cuda.synchronize()
+    want_dense = oracle.attention(wl.grid, wl.tile, c.q, c.k, c.v, ones)
+    assert_close(as_f64(host(got, c.q)), want_dense, "bf16", "wrapper dense")
+    sa.sparse_attn_destroy(att.h)
