@@ -372,6 +372,18 @@ class SparseAttention:
         sparse_attn_forward(self.h, q, k, v, o, self.ws, stream)
         return o
 
+    def close(self):
+        """Destroys the handle (host state); the torch buffers go with the object."""
+        if self.h is not None:
+            sparse_attn_destroy(self.h)
+            self.h = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
 
 def sparse_attn_tile_mass(h, q, k, ws, mass, stream=None):
     """Full-attention mass per tile pair into mass (device fp32 [heads, nT, nT])."""

@@ -320,4 +320,6 @@ def test_convenience_wrapper_matches_the_functional_calls():
     torch.cuda.synchronize()
     want_dense = oracle.attention(wl.grid, wl.tile, c.q, c.k, c.v, ones)
     assert_close(as_f64(host(got, c.q)), want_dense, "bf16", "wrapper dense")
-    sa.sparse_attn_destroy(att.h)
+    att.close()
+    assert att.h is None
+    att.close()  # a second close is a no-op
