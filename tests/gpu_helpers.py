@@ -80,3 +80,17 @@ def assert_lse_close(got, want, bound, what=""):
     print(f"{what} lse max_abs={float(err.max()) if fin.any() else 0.0:.3e} "
           f"max err/bound={worst:.3f}", flush=True)
     assert worst <= 1.0, what
+
+
+def mass_bound(q, k, want, N):
+    """Bound on |A_gpu - A_exact| for the tile mass, per entry: every term
+    exp(s q.k - LSE) is positive, so A carries a relative error of at most
+    the score error twice (d 2^-24 s |q| |k|, once in the score and once
+    through the LSE) plus n 2^-24 for fp32 sums of n positive terms (N keys
+    in the LSE, up to 128 x 128 terms per tile pair)."""
+    u = 2.0 ** -24
+    d = q.shape[-1]
+    qn = max(np.linalg.norm(as_f64(q[h]), axis=-1).max() for h in range(q.shape[0]))
+    kn = max(np.linalg.norm(as_f64(k[h]), axis=-1).max() for h in range(k.shape[0]))
+    rel = 2 * d * u * qn * kn / np.sqrt(d) + (N + 128 * 128) * u
+    return want * rel + 1e-12

@@ -15,7 +15,7 @@ import block_sparse_attention_major_amd as sa
 import oracle
 from workloads import f32_to_bf16_bits, make_workload
 
-from gpu_helpers import as_f64, assert_close, assert_lse_close, dev, host, lse_bound
+from gpu_helpers import as_f64, assert_close, assert_lse_close, dev, host, lse_bound, mass_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -211,3 +211,25 @@ def test_full_size_wan_shape_sampled():
     want = oracle.attention_rows(g1, t1, wl.q[:, seq], wl.k[:, seq], wl.v[:, seq], M, rows_seq)
     got = as_f64(host(o, wl.q).reshape(-1, d)[rows_raster])
     assert_close(got, want, "bf16", f"hilbert wan ({len(rows_raster)} sampled rows)")
+
+
+def test_tile_mass_on_hilbert_tiles():
+    """The full-attention tile mass on Hilbert tiles equals the oracle's on
+    the rank-ordered 1-D grid, within the mass bound."""
+    grid, tile, d, heads = (3, 20, 36), (1, 8, 16), 128, 2
+    N = int(np.prod(grid))
+    seq, g1, t1 = _seq_view(grid, tile)
+    q, k = (_rand((heads, N, d), s, "bf16") for s in (21, 22))
+    h = _handle(heads, d, grid, tile, "bf16")
+    nT = sa.sparse_attn_layout(h)["tiles"]
+    ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+    mass = torch.full((heads, nT, nT), -1.0, dtype=torch.float32, device="cuda")
+    print(f"hilbert tile mass grid={grid} tiles={nT}", flush=True)
+    sa.sparse_attn_tile_mass(h, dev(q), dev(k), ws, mass)
+    torch.cuda.synchronize()
+    got = mass.cpu().numpy().astype(np.float64)
+    want = oracle.tile_mass(g1, t1, q[:, seq], k[:, seq])
+    err = np.abs(got - want)
+    bound = mass_bound(q, k, want, N)
+    print(f"  max abs {err.max():.3e}, max err/bound {(err / bound).max():.3f}", flush=True)
+    assert np.all(err <= bound)

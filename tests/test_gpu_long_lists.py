@@ -20,7 +20,7 @@ import torch
 import block_sparse_attention_major_amd as sa
 import oracle
 
-from gpu_helpers import as_f64, assert_close, dev, host
+from gpu_helpers import as_f64, assert_close, assert_lse_close, dev, host, lse_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -78,8 +78,9 @@ def test_lists_longer_than_the_lds_stage():
 
     qd, kd, vd = dev(q), dev(k), dev(v)
     o = torch.full_like(qd, 0x7FC0)
+    lse = torch.full((HEADS, N), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
-    sa.sparse_attn_forward(h, qd, kd, vd, o, ws)
+    sa.sparse_attn_forward_lse(h, qd, kd, vd, o, lse, ws)
     torch.cuda.synchronize()
 
     frame = GRID[1] * GRID[2]
@@ -88,7 +89,14 @@ def test_lists_longer_than_the_lds_stage():
         pick(0, 0, 24), pick(0, 1, 24), pick(0, 5, 40), pick(1, 10, 24), pick(1, 11, 24),
         rng.choice(HEADS * N, 24, replace=False)])).astype(np.int64)
     print(f"  oracle on {len(rows)} sampled rows", flush=True)
-    want = oracle.attention_rows(GRID, TILE, q, k, v, M, rows)
+    want, want_lse = oracle.attention_rows(GRID, TILE, q, k, v, M, rows, lse=True)
     got = as_f64(host(o, q).reshape(-1, D)[rows])
     assert_close(got, want, "bf16", f"long lists ({len(rows)} sampled rows)")
+    # Every tile is full (128 tokens); features are below 2 in magnitude.
+    hh, n = rows // N, rows % N
+    tile_of = (n // frame) * NY * NX + ((n % frame) // GRID[2] // 8) * NX + (n % GRID[2]) // 16
+    kept = M[hh, tile_of].sum(axis=1) * 128
+    bound = lse_bound(as_f64(q.reshape(-1, D)[rows]), 2.0 * np.sqrt(D), kept, D, 1.0 / np.sqrt(D), "bf16",
+                      want_lse)
+    assert_lse_close(lse.cpu().numpy().reshape(-1)[rows].astype(np.float64), want_lse, bound, "long lists")
     sa.sparse_attn_destroy(h)
