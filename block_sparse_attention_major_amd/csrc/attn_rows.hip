@@ -14,7 +14,8 @@
 // Design (ours, for CDNA4; the pages give no kernel design):
 //  - One workgroup of 4 waves per (head, query tile); tile = 128 slots, each
 //    wave owns 32 query slots.  Two workgroups share a CU, so each SIMD runs
-//    two independent waves and overlaps one's softmax with the other's MFMAs.
+//    two independent waves and overlaps one's softmax with the other's MFMAs;
+//    a wave raises its issue priority for its softmax, which bounds the step.
 //    Workgroups follow the compiled longest-first order, remapped so each XCD
 //    (which owns its L2) takes contiguous chunks of it: neighbouring rows
 //    share key tiles.
@@ -120,41 +121,64 @@ __device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P,
 // transposed V [D][64], both swizzled.  The stage is 2 * D KB, moved as 1 KB
 // DMA blocks of 64 lanes x 16 bytes; LDS byte 16 l of a block receives lane
 // l's load, so each lane fetches the global chunk that the swizzle puts
-// there.  Wave w issues blocks [w * BPW, (w + 1) * BPW).
+// there.  Wave w moves blocks [w * BPW, (w + 1) * BPW): the first half of the
+// waves moves K, the second half V^T.
 template <int D>
-__device__ __forceinline__ void issue_stage(lds_char *stage, const uint16_t *__restrict__ Kp,
-                                            const uint16_t *__restrict__ Vt, const Layout &L, int h,
-                                            int j, int half, int wave, int lane)
+struct RowDma {
+    static constexpr int RCK = D / 8;                   // 16-byte chunks per K row
+    static constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
+    static constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
+    static_assert(KBLK % BPW == 0, "a wave moves K blocks or V^T blocks, not both");
+    __amdgpu_buffer_rsrc_t rsrc;  // K of head h, or V^T of head h (N_pad D 2 bytes)
+    bool is_v;                    // wave-uniform
+    int off[BPW];                 // byte offset of the lane's chunk within a stage
+};
+
+template <int D>
+__device__ __forceinline__ void make_row_dma(RowDma<D> &pl, const uint16_t *Kp, const uint16_t *Vt,
+                                             const Layout &L, int h, int wave, int lane)
 {
-    constexpr int RCK = D / 8;                   // 16-byte chunks per K row
-    constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
-    constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
-    // Raw buffers over head h's permuted K and transposed V (N_pad D 2
-    // bytes each, below 2^31 because the plan keeps heads * tiles^2 below
-    // 2^31); the stage is a uniform offset into them.
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Kp + (long long)h * L.Npad * D), 0, L.Npad * D * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Vt + (long long)h * L.nT * D * kTile), 0, L.Npad * D * 2, 0x00020000);
-    const int koff = (j * kTile + half * kStage) * D * 2;
-    const int voff = (j * D * kTile + half * kStage) * 2;
+    constexpr int RCK = RowDma<D>::RCK, KBLK = RowDma<D>::KBLK, BPW = RowDma<D>::BPW;
+    pl.is_v = wave * BPW >= KBLK;
+    const char *base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
+                               : (const char *)(Kp + (long long)h * L.Npad * D);
+    // Raw buffer over one head's K (or V^T): N_pad D 2 bytes, below 2^31
+    // because the plan keeps heads * tiles^2 below 2^31, so the stage's
+    // byte offset (scalar) and the lane's offset in it (vector) both fit 32
+    // bits.  Word 3 is the gfx9 raw 32-bit data format.
+    pl.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, L.Npad * D * 2, 0x00020000);
     const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
-        const int blk = wave * BPW + t;  // wave-uniform
-        const int kb = blk < KBLK ? blk : blk - KBLK;
+        const int blk = wave * BPW + t;
+        const int kb = pl.is_v ? blk - KBLK : blk;
         const int line = 4 * kb + line_in_blk;
         const int logical = phys ^ (line & 15);
-        auto *dst = (void __attribute__((address_space(3))) *)(stage + blk * 1024);
-        if (blk < KBLK) {
+        if (!pl.is_v) {
             constexpr int RPL = 16 / RCK;
             const int row = RPL * line + logical / RCK, c = logical % RCK;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, dst, 16, row * D * 2 + 16 * c, koff, 0, 0);
+            pl.off[t] = row * D * 2 + 16 * c;
         } else {
             const int dv = 2 * line + (logical >> 3), c = logical & 7;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, dst, 16, dv * kTile * 2 + 16 * c, voff, 0, 0);
+            pl.off[t] = dv * kTile * 2 + 16 * c;
         }
     }
+}
+
+// Issue this wave's DMA blocks of stage (key tile j, half `half`) into the
+// stage buffer at `stage`.  j and wave are wave-uniform (read with
+// readfirstlane), so the stage offset and the LDS destinations are scalars
+// and the eight copies issue without branches.
+template <int D>
+__device__ __forceinline__ void issue_stage(const RowDma<D> &pl, lds_char *stage, int j, int half, int wave)
+{
+    constexpr int BPW = RowDma<D>::BPW;
+    const int soff = pl.is_v ? (j * D * kTile + half * kStage) * 2 : (j * kTile + half * kStage) * D * 2;
+    lds_char *dst = stage + wave * BPW * 1024;
+#pragma unroll
+    for (int t = 0; t < BPW; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pl.rsrc, (__attribute__((address_space(3))) void *)(dst + t * 1024),
+                                                 16, pl.off[t], soff, 0, 0);
 }
 
 // The per-wave state of one query block: 32 queries x D features.
@@ -194,6 +218,11 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
             s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi)), qf[ks], s0, 0, 0, 0);
     }
+    // From here to the P V products the wave runs its softmax at raised
+    // issue priority: the other workgroup's wave on this SIMD is then most
+    // often in its matrix products, and the exponentials, which bound the
+    // step, get the issue slots first.
+    __builtin_amdgcn_s_setprio(2);
     if (kv < kStage) {
         // Key 16 (jj / 8) + 8 hi + jj % 8 of each half is past the end when
         // 16 (jj / 8) + jj % 8 >= kv - 8 hi (one register, constants inline).
@@ -249,6 +278,7 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
         st.l = row_sum_bf16(p1a, row_sum_bf16(p1b, st.l));
     }
     // O^T += V^T P^T: A operand = V^T rows 32 nb + l32, keys in 16-key steps.
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
         st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -289,7 +319,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
     uint16_t *__restrict__ Op = (uint16_t *)P.o;
     const int *__restrict__ cols = P.rows.cols;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keep it scalar
     const int l32 = lane & 31, hi = lane >> 5;
 
     // XCD-aware remap: workgroup b runs on XCD b % 8; give each XCD
@@ -362,13 +393,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
         __syncthreads();
     };
 
+    RowDma<D> dma;
+    make_row_dma<D>(dma, Kp, Vt, L, h, wave, lane);
+
     // Stage cursor: key tile idx (id j, c real tokens) and which half of it.
     int idx = beg, half = 0, j = 0, c = 0;
     if (idx < end) {
         fill_list(beg);
-        j = clist[0];
+        j = __builtin_amdgcn_readfirstlane(clist[0]);
         c = tile_tokens(L, P, j);
-        issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, 0, wave, lane);
+        issue_stage<D>(dma, (lds_char *)buf0, j, 0, wave);
     }
     const int prow = key_of_mfma_row(l32);
 
@@ -384,7 +418,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
                     __syncthreads();  // every wave is done reading the list
                     fill_list(idx);
                 }
-                j = clist[idx - list_base];
+                j = __builtin_amdgcn_readfirstlane(clist[idx - list_base]);
                 c = tile_tokens(L, P, j);
             }
         }
@@ -398,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
             __syncthreads();  // buf0 complete; buf1 free
             advance();
             if (idx < end)
-                issue_stage<D>((lds_char *)buf1, Kp, Vt, L, h, j, half, wave, lane);
+                issue_stage<D>(dma, (lds_char *)buf1, j, half, wave);
             if (wave_active)
                 attend_stage<D>(buf0, qf, kv, sl2, prow, l32, hi, st);
         }
@@ -411,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
             __syncthreads();  // buf1 complete; buf0 free
             advance();
             if (idx < end)
-                issue_stage<D>((lds_char *)buf0, Kp, Vt, L, h, j, half, wave, lane);
+                issue_stage<D>(dma, (lds_char *)buf0, j, half, wave);
             if (wave_active)
                 attend_stage<D>(buf1, qf, kv, sl2, prow, l32, hi, st);
         }
