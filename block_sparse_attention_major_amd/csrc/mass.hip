@@ -19,7 +19,8 @@
 // stays in registers as the B operand); lane l then holds the scores of
 // query l % 32 against 16 keys of each 32-key block.  Per key tile, each
 // wave's pass-2 partial sum goes to LDS and one thread per query tile adds
-// the four after the next barrier.
+// the four after the next barrier.  Two workgroups share a CU; a wave raises
+// its issue priority for the exponentials of each block.
 #include "common.h"
 
 namespace sa {
@@ -184,6 +185,10 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
             f32x16 s = block_scores<D>(Ks, kb, qf, l32, hi);
             if (kb * 32 + 32 > cj)
                 mask_tail(s, kb, cj, hi);
+            // The exponentials of a block run at raised issue priority: the
+            // other workgroup's waves on this SIMD are then most often in
+            // their matrix products, and the exponentials bound the loop.
+            __builtin_amdgcn_s_setprio(2);
             float mx = s[0];
 #pragma unroll
             for (int r = 1; r < 16; ++r)
@@ -196,6 +201,7 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
                 for (int r = 0; r < 16; ++r)
                     l += __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -m));
             }
+            __builtin_amdgcn_s_setprio(0);
         }
     };
     // Pass 2: the partial sums of tile j go to part[j & 1] and are added up
@@ -217,9 +223,11 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
                 f32x16 s = block_scores<D>(Ks, kb, qf, l32, hi);
                 if (kb * 32 + 32 > cj)
                     mask_tail(s, kb, cj, hi);
+                __builtin_amdgcn_s_setprio(2);
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc += __builtin_amdgcn_exp2f(fmaf(s[r], scale_log2, -lse2));
+                __builtin_amdgcn_s_setprio(0);
             }
         }
         acc = wave_sum(q_real ? acc : 0.f);
