@@ -147,6 +147,25 @@ class Handle:
     def __init__(self, ptr, cfg):
         self.ptr = ptr
         self.cfg = cfg
+        self._sizes = None
+
+    @property
+    def sizes(self):
+        """Byte sizes of the caller buffers, from the planned layout."""
+        if self._sizes is None:
+            L = sparse_attn_layout(self)
+            heads, d = self.cfg.heads, self.cfg.head_dim
+            elem = 4 if self.cfg.dtype == SPARSE_ATTN_F32 else 2
+            N, nT, slots = L["tokens"], L["tiles"], L["slots"]
+            self._sizes = {
+                "elem": elem, "heads": heads, "tiles": nT, "pairs": L["pairs"],
+                "io": heads * N * d * elem,          # q, k, v, o in raster order
+                "slots": heads * slots * d * elem,   # a tile-major tensor
+                "lse": heads * N * 4,
+                "bitmap": heads * nT * nT,
+                "mass": heads * nT * nT * 4,
+            }
+        return self._sizes
 
     def __del__(self):
         if getattr(self, "ptr", None):
@@ -170,6 +189,39 @@ def _dptr(t, name):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t.data_ptr()
+
+
+def _sized(t, name, nbytes, elem=None, at_least=False):
+    """Device pointer of t after checking that it holds exactly (or, with
+    at_least, at least) nbytes bytes of elements of size elem: the C ABI
+    takes no sizes for these buffers, so a mis-sized tensor is refused here,
+    before anything is enqueued."""
+    if t is None or isinstance(t, int):
+        return _dptr(t, name)
+    if elem is not None and t.element_size() != elem:
+        raise ValueError(f"{name}: elements of {t.element_size()} bytes, expected {elem}")
+    got = t.numel() * t.element_size()
+    if (got < nbytes) if at_least else (got != nbytes):
+        raise ValueError(f"{name}: {got} bytes, expected {'at least ' if at_least else ''}{nbytes}")
+    return _dptr(t, name)
+
+
+def _host_heads(a, name, heads):
+    """A host int32 array with one entry per head."""
+    a = np.ascontiguousarray(a, dtype=np.int32).reshape(-1)
+    if a.shape[0] != heads:
+        raise ValueError(f"{name}: {a.shape[0]} entries, expected one per head ({heads})")
+    return a
+
+
+def _host_groups(groups, gph, heads):
+    """Window groups [G, 6] and groups per head, checked against each other
+    and the head count."""
+    g = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 6)
+    gph = _host_heads(gph, "groups_per_head", heads)
+    if g.shape[0] != int(gph.astype(np.int64).sum()):
+        raise ValueError(f"groups: {g.shape[0]} rows, expected sum(groups_per_head) = {int(gph.sum())}")
+    return g, gph
 
 
 def _stream(stream):
@@ -251,10 +303,9 @@ def sparse_attn_set_mask(h, mask_buf, bitmap=None, groups=None, groups_per_head=
     keep = []
     if bitmap is not None:
         m.kind = SPARSE_ATTN_MASK_BITMAP
-        m.bitmap = _dptr(bitmap, "bitmap")
+        m.bitmap = _sized(bitmap, "bitmap", h.sizes["bitmap"], elem=1)
     else:
-        g = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 6)
-        gph = np.ascontiguousarray(groups_per_head, dtype=np.int32)
+        g, gph = _host_groups(groups, groups_per_head, h.cfg.heads)
         keep += [g, gph]
         m.kind = SPARSE_ATTN_MASK_DUAL_WINDOW
         m.groups = g.ctypes.data
@@ -265,30 +316,38 @@ def sparse_attn_set_mask(h, mask_buf, bitmap=None, groups=None, groups_per_head=
     del keep
 
 
+def _io(h, t, name):
+    return _sized(t, name, h.sizes["io"], elem=h.sizes["elem"])
+
+
+def _lse(h, t):
+    return _sized(t, "lse", h.sizes["lse"], elem=4)
+
+
 def sparse_attn_forward(h, q, k, v, o, ws, stream=None):
-    _check(_lib.sparse_attn_forward(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"), _dptr(o, "o"),
+    _check(_lib.sparse_attn_forward(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _io(h, v, "v"), _io(h, o, "o"),
                                     _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
 
 
 def sparse_attn_forward_lse(h, q, k, v, o, lse, ws, stream=None):
     """Forward that also writes lse (device fp32 [heads, N], or None)."""
-    _check(_lib.sparse_attn_forward_lse(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"),
-                                        _dptr(o, "o"), _dptr(lse, "lse"), _dptr(ws, "ws"),
+    _check(_lib.sparse_attn_forward_lse(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _io(h, v, "v"),
+                                        _io(h, o, "o"), _lse(h, lse), _dptr(ws, "ws"),
                                         _nbytes(ws), _stream(stream)), h)
 
 
 def sparse_attn_permute_kv(h, k, v, ws, stream=None):
-    _check(_lib.sparse_attn_permute_kv(h.ptr, _dptr(k, "k"), _dptr(v, "v"), _dptr(ws, "ws"),
+    _check(_lib.sparse_attn_permute_kv(h.ptr, _io(h, k, "k"), _io(h, v, "v"), _dptr(ws, "ws"),
                                        _nbytes(ws), _stream(stream)), h)
 
 
 def sparse_attn_attend_raster(h, q, o, ws, lse=None, stream=None):
-    _check(_lib.sparse_attn_attend_raster(h.ptr, _dptr(q, "q"), _dptr(o, "o"), _dptr(lse, "lse"),
+    _check(_lib.sparse_attn_attend_raster(h.ptr, _io(h, q, "q"), _io(h, o, "o"), _lse(h, lse),
                                           _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
 
 
 def sparse_attn_permute_inputs(h, q, k, v, ws, stream=None):
-    _check(_lib.sparse_attn_permute_inputs(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(v, "v"),
+    _check(_lib.sparse_attn_permute_inputs(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _io(h, v, "v"),
                                            _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
 
 
@@ -297,38 +356,48 @@ def sparse_attn_attend(h, ws, stream=None):
 
 
 def sparse_attn_unpermute_output(h, ws, o, stream=None):
-    _check(_lib.sparse_attn_unpermute_output(h.ptr, _dptr(ws, "ws"), _nbytes(ws), _dptr(o, "o"),
+    _check(_lib.sparse_attn_unpermute_output(h.ptr, _dptr(ws, "ws"), _nbytes(ws), _io(h, o, "o"),
                                              _stream(stream)), h)
 
 
 def sparse_attn_permute(h, src, dst, layout=SPARSE_ATTN_LAYOUT_ROWS, stream=None):
-    _check(_lib.sparse_attn_permute(h.ptr, _dptr(src, "src"), _dptr(dst, "dst"), int(layout),
+    _check(_lib.sparse_attn_permute(h.ptr, _io(h, src, "src"),
+                                    _sized(dst, "dst", h.sizes["slots"], elem=h.sizes["elem"]), int(layout),
                                     _stream(stream)), h)
 
 
 def sparse_attn_unpermute(h, src, dst, stream=None):
-    _check(_lib.sparse_attn_unpermute(h.ptr, _dptr(src, "src"), _dptr(dst, "dst"), _stream(stream)), h)
+    _check(_lib.sparse_attn_unpermute(h.ptr, _sized(src, "src", h.sizes["slots"], elem=h.sizes["elem"]),
+                                      _io(h, dst, "dst"), _stream(stream)), h)
 
 
 def sparse_attn_read_index_lists(h, row_ptr, cols, order, stream=None):
-    _check(_lib.sparse_attn_read_index_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
+    R = h.sizes["heads"] * h.sizes["tiles"]
+    _check(_lib.sparse_attn_read_index_lists(h.ptr, _sized(row_ptr, "row_ptr", 4 * (R + 1), elem=4, at_least=True),
+                                             _sized(cols, "cols", 0, elem=4, at_least=True),
                                              cols.numel() if cols is not None else 0,
-                                             _dptr(order, "order"), _stream(stream)), h)
+                                             _sized(order, "order", 4 * R, elem=4, at_least=True),
+                                             _stream(stream)), h)
 
 
 def sparse_attn_select_topk(h, k_per_head, ws, bitmap, stream=None):
     """Top-k tile bitmap from the permuted Q and K in ws (run
     sparse_attn_permute_inputs on ws first); bitmap: device uint8
     [heads, nT, nT]."""
-    kh = (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
-    _check(_lib.sparse_attn_select_topk(h.ptr, kh, _dptr(ws, "ws"), _nbytes(ws),
-                                        _dptr(bitmap, "bitmap"), _stream(stream)), h)
+    kh = _host_heads([int(x) for x in k_per_head], "k_per_head", h.cfg.heads)
+    _check(_lib.sparse_attn_select_topk(h.ptr, kh.ctypes.data, _dptr(ws, "ws"), _nbytes(ws),
+                                        _sized(bitmap, "bitmap", h.sizes["bitmap"], elem=1),
+                                        _stream(stream)), h)
 
 
 def sparse_attn_read_pair_lists(h, row_ptr, cols, order, flag, stream=None):
-    _check(_lib.sparse_attn_read_pair_lists(h.ptr, _dptr(row_ptr, "row_ptr"), _dptr(cols, "cols"),
+    mfma = sparse_attn_layout(h)["kernel"] == SPARSE_ATTN_KERNEL_MFMA_BF16
+    R = h.sizes["heads"] * h.sizes["pairs"] if mfma else 0  # (UNSUPPORTED otherwise)
+    _check(_lib.sparse_attn_read_pair_lists(h.ptr, _sized(row_ptr, "row_ptr", 4 * (R + 1), elem=4, at_least=True),
+                                            _sized(cols, "cols", 0, elem=4, at_least=True),
                                             cols.numel() if cols is not None else 0,
-                                            _dptr(order, "order"), _dptr(flag, "flag"),
+                                            _sized(order, "order", 4 * R, elem=4, at_least=True),
+                                            _sized(flag, "flag", 4 * R, elem=4, at_least=True),
                                             _stream(stream)), h)
 
 
@@ -387,19 +456,21 @@ class SparseAttention:
 
 def sparse_attn_tile_mass(h, q, k, ws, mass, stream=None):
     """Full-attention mass per tile pair into mass (device fp32 [heads, nT, nT])."""
-    _check(_lib.sparse_attn_tile_mass(h.ptr, _dptr(q, "q"), _dptr(k, "k"), _dptr(ws, "ws"), _nbytes(ws),
-                                      _dptr(mass, "mass"), _stream(stream)), h)
+    _check(_lib.sparse_attn_tile_mass(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _dptr(ws, "ws"), _nbytes(ws),
+                                      _sized(mass, "mass", h.sizes["mass"], elem=4), _stream(stream)), h)
 
 
 def sparse_attn_search_windows(h, mass, groups, groups_per_head, tau, lam=float("inf")):
     """Host search.  mass: host float32 [heads, nT, nT]; groups: int32 [G, 6]
     rows (dt_lo, dt_hi, ...) (windows ignored); returns (groups [G, 6] with
     the searched windows, recall [heads], cost [heads])."""
+    heads = h.cfg.heads
+    nT = h.sizes["tiles"]
     m = np.ascontiguousarray(mass, dtype=np.float32)
-    g = np.ascontiguousarray(groups, dtype=np.int32).reshape(-1, 6)
-    gph = np.ascontiguousarray(groups_per_head, dtype=np.int32)
+    if m.size != heads * nT * nT:
+        raise ValueError(f"mass: {m.size} values, expected heads * nT * nT = {heads * nT * nT}")
+    g, gph = _host_groups(groups, groups_per_head, heads)
     out = np.zeros_like(g)
-    heads = gph.shape[0]
     rec = np.zeros(heads)
     cst = np.zeros(heads)
     _check(_lib.sparse_attn_search_windows(h.ptr, m.ctypes.data, g.ctypes.data, gph.ctypes.data,

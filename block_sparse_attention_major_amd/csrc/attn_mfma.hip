@@ -45,87 +45,31 @@
 //    k-steps ahead).
 //  - LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
 //    16 distinct chunk positions per 16 lanes.
-//  - Online softmax in fp32 and exp2 with a lazily moved running max; row
-//    sums are taken from the bf16 probabilities with v_dot2.
+//  - Online softmax in fp32 and exp2 against a running reference that is
+//    moved only on a rare wave-uniform redo (no row maximum per stage; see
+//    online_softmax in mfma_util.h); row sums are taken from the bf16
+//    probabilities with v_dot2.
 //  - Each lane reads its query row of Q and writes its row of O either in
 //    the caller's raster tensors (the forward: the Q permute and O
 //    unpermute are fused here, real slots only) or in the tile-major
 //    workspace; optionally it writes the query's log-sum-exp, m + log2 l
 //    scaled back to natural log, from the same running max and row sum.
-#include "common.h"
+#include "mfma_util.h"
 
 namespace sa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) char lds_char;
+using namespace mfma;
 
 constexpr int kWaves = 8;    // waves 0-3: first query tile of the pair, 4-7: second
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 128;   // slots per tile
-constexpr int kStage = 64;   // keys per LDS stage
 constexpr int kList = 2048;  // pair-list entries staged in LDS at a time
 
-// Probabilities are kept below 2^kLazy (see the online softmax below).
-constexpr float kLazy = 8.0f;
-
-// Byte offset of 16-byte chunk c of row `row` in an LDS block whose rows hold
-// RC chunks.  Rows are packed into 256-byte lines; the chunk index is XORed
-// with the line index so 16 consecutive rows read at one column hit 16
-// different chunk positions.
-template <int RC>
-__device__ __forceinline__ int lds_off(int row, int c)
-{
-    constexpr int RPL = 16 / RC;
-    const int line = row / RPL;
-    const int logical = (row % RPL) * RC + c;
-    return line * 256 + ((logical ^ (line & 15)) << 4);
-}
-
-// Key row fed to MFMA row m of a 32-key subtile.  With this order, result
-// register j of lane l holds key 16 (j / 8) + 8 (l / 32) + j % 8, which is
-// the B-operand order of the P V^T product.
-__device__ __forceinline__ int key_of_mfma_row(int m)
-{
-    const int a = m >> 3, b = (m >> 2) & 1, c = m & 3;
-    return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Lanes l and l ^ 32 hold the two halves of one query row.
-__device__ __forceinline__ float half_max(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// acc + sum of the 8 bf16 values of p (two per v_dot2 with a vector of ones).
-__device__ __forceinline__ float row_sum_bf16(bf16x8 p, float acc)
-{
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
-}
-
-// Real tokens of tile j (clipped at the far edges of the grid).
+// Real tokens of tile j.
 __device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P, int j)
 {
-    const int a = (int)fast_div((uint32_t)j, P.div_plane);
-    const int rem = j - a * L.ny * L.nx;
-    const int b = (int)fast_div((uint32_t)rem, P.div_row);
-    const int e = rem - b * L.nx;
-    return min(L.tt, L.T - a * L.tt) * min(L.th, L.H - b * L.th) * min(L.tw, L.W - e * L.tw);
+    return mfma::tile_tokens(L, P.div_plane, P.div_row, j);
 }
 
 // Geometry of one stage (64 keys of one key tile) in LDS: K rows [64][D] and
@@ -199,25 +143,6 @@ __device__ __forceinline__ void issue_block(const DmaPlan<D> &pl, char *Kd, char
                                              pl.off[t], soff, 0, 0);
 }
 
-// The per-wave state of one query block: 32 queries x D features.
-template <int D>
-struct RowState {
-    f32x16 acc[D / 32];
-    float m, l;  // running max (log2 units) and partial row sum of this lane
-};
-
-// Scores of this wave's 32 queries against the keys of one stage, S^T =
-// K Q^T as two 32-key halves (result register j of lane l: key
-// 16 (j / 8) + 8 (l / 32) + j % 8 of the half, query l % 32).
-struct Scores {
-    f32x16 s0, s1;
-};
-// Probabilities in bf16, in the B-operand order of O^T += V^T P^T: 16-key
-// steps 0..3 of the stage.
-struct Probs {
-    bf16x8 p[4];
-};
-
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
@@ -289,71 +214,8 @@ __device__ __forceinline__ void qk_stage(Scores &S, const char *Ks, const bf16x8
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
         }
     }
-    if (kv < kStage) {
-        // Key 16 (jj / 8) + 8 hi + jj % 8 of each half is past the end when
-        // 16 (jj / 8) + jj % 8 >= kv - 8 hi (one register, constants inline).
-        const int lim = kv - 8 * hi;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int c = 16 * (jj >> 3) + (jj & 7);
-            if (c >= lim)
-                S.s0[jj] = -INFINITY;
-            if (32 + c >= lim)
-                S.s1[jj] = -INFINITY;
-        }
-    }
-}
-
-// Online softmax step: scores -> bf16 probabilities, running max and row sum
-// updated, accumulator rescaled when the max moves.  dma(t) as in qk_stage,
-// spread over the exponentials.
-template <int D, typename Dma>
-__device__ __forceinline__ void softmax_stage(Probs &P, const Scores &S, int kv, float sl2,
-                                              RowState<D> &st, Dma &&dma)
-{
-    constexpr int NB = D / 32;
-    constexpr int BPW = Stage<D>::BPW;
-    static_assert(BPW <= 4, "one DMA block per 16-key step at most");
-    const bool two = kv > 32;
-    float mx = S.s0[0];
-#pragma unroll
-    for (int jj = 1; jj < 16; ++jj)
-        mx = fmaxf(mx, S.s0[jj]);
-    if (two) {
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-            mx = fmaxf(mx, S.s1[jj]);
-    }
-    // Running max in log2 units, moved lazily: only when some row's new
-    // maximum exceeds it by more than kLazy, so the rescale of the
-    // accumulator is a rare wave-uniform branch.  Numerator and denominator
-    // share the max, so the result does not depend on it; probabilities stay
-    // below 2^kLazy.
-    const float t = half_max(mx) * sl2;
-    if (__ballot(t > st.m + kLazy)) {
-        const float m_new = fmaxf(st.m, t);
-        const float alpha = exp2_fast(st.m - m_new);
-        st.m = m_new;
-        st.l *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                st.acc[nb][jj] *= alpha;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (q < 2 || two) {
-            const f32x16 &src = q < 2 ? S.s0 : S.s1;
-            const int o = (q & 1) * 8;
-#pragma unroll
-            for (int jj = 0; jj < 8; ++jj)
-                P.p[q][jj] = (__bf16)exp2_fast(fmaf(src[o + jj], sl2, -st.m));
-            st.l = row_sum_bf16(P.p[q], st.l);
-        }
-        if (q < BPW)
-            dma(q);
-    }
+    if (kv < kStage)
+        mask_stage_tail(S, kv, hi);
 }
 
 // O^T += V^T P^T over the stage whose V^T is at Vs (kv real keys).
@@ -399,23 +261,6 @@ __device__ __forceinline__ void pv_stage(const char *Vs, const int (&vofs)[4], c
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NB, 0);
         }
     }
-}
-
-// s_waitcnt on this wave's vector-memory counter only (gfx9 encoding: vmcnt
-// in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier that waits for this wave's LDS operations but leaves its
-// DMA copies in flight (__syncthreads would drain those as well).
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
 }
 
 template <int D>
@@ -655,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         for (int t = 0; t < BPW; ++t)
             issue_block<D>(plan, Kn, Vn, src, wave, t);
         if (attends(dcur))
-            softmax_stage<D>(Pr, S, dcur & 255, sl2, st, [](int) {});
+            online_softmax<D>(Pr, S, dcur & 255, sl2, st);
         return dcur != 0;
     };
     if (side == 1)
@@ -680,31 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         lds_barrier();  // pairs with B's extra barrier: both groups pass the same count
     wait_vmcnt<0>();  // no copy may land after the workgroup ends
 
-    // half_sum exchanges lanes l and l ^ 32, so it runs with the whole wave.
-    const float lt = wave_active ? half_sum(st.l) : 0.f;
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    // st.m is in log2 units and st.l sums exp2(score * log2 e - st.m).
-    if (lse_at)
-        *lse_at = lt > 0.f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
-    if (q_io) {
-        uint16_t *orow = Op + qrow * D;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // O^T accumulator register 4 g + u of lane l holds feature
-                // 32 nb + 8 g + 4 hi + u of query l32.
-                union {
-                    __bf16 b[4];
-                    uint2 u;
-                } pk;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    pk.b[u] = (__bf16)(st.acc[nb][4 * g + u] * inv);
-                *(uint2 *)(orow + 32 * nb + 8 * g + 4 * hi) = pk.u;
-            }
-        }
-    }
+    finish_rows<D>(st, wave_active, lse_at, q_io ? Op + qrow * D : nullptr, hi);
 }
 
 }  // namespace

@@ -37,84 +37,28 @@
 //    stage), so V^T operand reads are plain 16-byte LDS reads.
 //  - LDS rows are XOR-swizzled in 16-byte chunks so the MFMA operand reads hit
 //    16 distinct chunk positions per 16 lanes.
-//  - Online softmax in fp32 and exp2 with a lazily moved running max; row
-//    sums are taken from the bf16 probabilities with v_dot2.
+//  - Online softmax in fp32 and exp2 against a running reference that is
+//    moved only on a rare wave-uniform redo (no row maximum per stage; see
+//    online_softmax in mfma_util.h); row sums are taken from the bf16
+//    probabilities with v_dot2.
 //  - Q and O rows go to the caller's raster tensors or the tile-major
 //    workspace, and the log-sum-exp is written on request, as in the pair
 //    kernel.
-#include "common.h"
+#include "mfma_util.h"
 
 namespace sa {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) char lds_char;
+using namespace mfma;
 
 constexpr int kThreads = 256;
-constexpr int kTile = 128;   // slots per tile
-constexpr int kStage = 64;   // keys per LDS stage
 constexpr int kList = 2048;  // key-tile ids staged in LDS at a time
 
-// Probabilities are kept below 2^kLazy (see the online softmax below).
-constexpr float kLazy = 8.0f;
-
-// Byte offset of 16-byte chunk c of row `row` in an LDS block whose rows hold
-// RC chunks.  Rows are packed into 256-byte lines; the chunk index is XORed
-// with the line index so 16 consecutive rows read at one column hit 16
-// different chunk positions.
-template <int RC>
-__device__ __forceinline__ int lds_off(int row, int c)
-{
-    constexpr int RPL = 16 / RC;
-    const int line = row / RPL;
-    const int logical = (row % RPL) * RC + c;
-    return line * 256 + ((logical ^ (line & 15)) << 4);
-}
-
-// Key row fed to MFMA row m of a 32-key subtile.  With this order, result
-// register j of lane l holds key 16 (j / 8) + 8 (l / 32) + j % 8, which is
-// the B-operand order of the P V^T product.
-__device__ __forceinline__ int key_of_mfma_row(int m)
-{
-    const int a = m >> 3, b = (m >> 2) & 1, c = m & 3;
-    return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
-}
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Lanes l and l ^ 32 hold the two halves of one query row.
-__device__ __forceinline__ float half_max(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_sum(float x)
-{
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// acc + sum of the 8 bf16 values of p (two per v_dot2 with a vector of ones).
-__device__ __forceinline__ float row_sum_bf16(bf16x8 p, float acc)
-{
-    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
-}
-
-// Real tokens of tile j (clipped at the far edges of the grid).
+// Real tokens of tile j.
 __device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P, int j)
 {
-    const int a = (int)fast_div((uint32_t)j, P.div_plane);
-    const int rem = j - a * L.ny * L.nx;
-    const int b = (int)fast_div((uint32_t)rem, P.div_row);
-    const int e = rem - b * L.nx;
-    return min(L.tt, L.T - a * L.tt) * min(L.th, L.H - b * L.th) * min(L.tw, L.W - e * L.tw);
+    return mfma::tile_tokens(L, P.div_plane, P.div_row, j);
 }
 
 // One stage (64 keys, half `half` of key tile j) in LDS: K rows [64][D] then
@@ -181,13 +125,6 @@ __device__ __forceinline__ void issue_stage(const RowDma<D> &pl, lds_char *stage
                                                  16, pl.off[t], soff, 0, 0);
 }
 
-// The per-wave state of one query block: 32 queries x D features.
-template <int D>
-struct RowState {
-    f32x16 acc[D / 32];
-    float m, l;  // running max (log2 units) and partial row sum of this lane
-};
-
 // Attention of this wave's 32 queries to the kv real keys (1..64) of the
 // stage held in LDS at Ks (K) and Ks + K_BYTES (V^T).
 template <int D>
@@ -198,7 +135,8 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
     constexpr int K_BYTES = kStage * D * 2;
     const char *Vs = Ks + K_BYTES;
     const bool two = kv > 32;
-    f32x16 s0, s1;
+    Scores S;
+    f32x16 &s0 = S.s0, &s1 = S.s1;
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) {
         s0[jj] = 0.f;
@@ -223,60 +161,11 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
     // often in its matrix products, and the exponentials, which bound the
     // step, get the issue slots first.
     __builtin_amdgcn_s_setprio(2);
-    if (kv < kStage) {
-        // Key 16 (jj / 8) + 8 hi + jj % 8 of each half is past the end when
-        // 16 (jj / 8) + jj % 8 >= kv - 8 hi (one register, constants inline).
-        const int lim = kv - 8 * hi;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            const int c = 16 * (jj >> 3) + (jj & 7);
-            if (c >= lim)
-                s0[jj] = -INFINITY;
-            if (32 + c >= lim)
-                s1[jj] = -INFINITY;
-        }
-    }
-    float mx = s0[0];
-#pragma unroll
-    for (int jj = 1; jj < 16; ++jj)
-        mx = fmaxf(mx, s0[jj]);
-    if (two) {
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj)
-            mx = fmaxf(mx, s1[jj]);
-    }
-    // Running max in log2 units, moved lazily: only when some row's new
-    // maximum exceeds it by more than kLazy, so the rescale of the
-    // accumulator is a rare wave-uniform branch.  Numerator and denominator
-    // share the max, so the result does not depend on it; probabilities stay
-    // below 2^kLazy.
-    const float t = half_max(mx) * sl2;
-    if (__ballot(t > st.m + kLazy)) {
-        const float m_new = fmaxf(st.m, t);
-        const float alpha = exp2_fast(st.m - m_new);
-        st.m = m_new;
-        st.l *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                st.acc[nb][jj] *= alpha;
-    }
-    bf16x8 p0a, p0b, p1a, p1b;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-        p0a[jj] = (__bf16)exp2_fast(fmaf(s0[jj], sl2, -st.m));
-        p0b[jj] = (__bf16)exp2_fast(fmaf(s0[jj + 8], sl2, -st.m));
-    }
-    st.l = row_sum_bf16(p0a, row_sum_bf16(p0b, st.l));
-    if (two) {
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-            p1a[jj] = (__bf16)exp2_fast(fmaf(s1[jj], sl2, -st.m));
-            p1b[jj] = (__bf16)exp2_fast(fmaf(s1[jj + 8], sl2, -st.m));
-        }
-        st.l = row_sum_bf16(p1a, row_sum_bf16(p1b, st.l));
-    }
+    if (kv < kStage)
+        mask_stage_tail(S, kv, hi);
+    Probs Pr;
+    online_softmax<D>(Pr, S, kv, sl2, st);
+    const bf16x8 &p0a = Pr.p[0], &p0b = Pr.p[1], &p1a = Pr.p[2], &p1b = Pr.p[3];
     // O^T += V^T P^T: A operand = V^T rows 32 nb + l32, keys in 16-key steps.
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
@@ -301,7 +190,7 @@ __device__ __forceinline__ void attend_stage(const char *Ks, const bf16x8 (&qf)[
 
 // Wait for this wave's outstanding vector-memory operations (the stage DMA),
 // leaving LDS and scalar counters alone.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem() { wait_vmcnt<0>(); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnParams P)
@@ -451,32 +340,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_rows_kernel(Layout L, AttnPa
         }
     }
 
-    if (wave_active) {
-        const float lt = half_sum(st.l);
-        const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        // st.m is in log2 units and st.l sums exp2(score * log2 e - st.m).
-        if (lse_at)
-            *lse_at = lt > 0.f ? (st.m + log2f(lt)) * kLn2 : -INFINITY;
-        if (!q_io)
-            return;
-        uint16_t *orow = Op + qrow * D;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                // O^T accumulator register 4 g + u of lane l holds feature
-                // 32 nb + 8 g + 4 hi + u of query l32.
-                union {
-                    __bf16 b[4];
-                    uint2 u;
-                } pk;
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    pk.b[u] = (__bf16)(st.acc[nb][4 * g + u] * inv);
-                *(uint2 *)(orow + 32 * nb + 8 * g + 4 * hi) = pk.u;
-            }
-        }
-    }
+    if (wave_active)
+        finish_rows<D>(st, true, lse_at, q_io ? Op + qrow * D : nullptr, hi);
 }
 
 }  // namespace

@@ -21,7 +21,7 @@
 // wave's pass-2 partial sum goes to LDS and one thread per query tile adds
 // the four after the next barrier.  Two workgroups share a CU; a wave raises
 // its issue priority for the exponentials of each block.
-#include "common.h"
+#include "mfma_util.h"
 
 namespace sa {
 
@@ -31,8 +31,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTileRows = 128;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace mfma;
 
 // Sum over the 64 lanes of a wave.
 __device__ __forceinline__ float wave_sum(float x)
@@ -41,18 +40,6 @@ __device__ __forceinline__ float wave_sum(float x)
     for (int o = 32; o >= 1; o >>= 1)
         x += __shfl_xor(x, o);
     return x;
-}
-
-// Byte offset of 16-byte chunk c of row `row` in a tile whose rows hold RC
-// chunks: rows are packed into 256-byte lines and the chunk index is XORed
-// with the line index.
-template <int RC>
-__device__ __forceinline__ int lds_off(int row, int c)
-{
-    constexpr int RPL = 16 / RC;
-    const int line = row / RPL;
-    const int logical = (row % RPL) * RC + c;
-    return line * 256 + ((logical ^ (line & 15)) << 4);
 }
 
 // Scores S^T of 32 keys (rows kb*32.. of the staged tile) against this
@@ -96,14 +83,7 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, char *dst, 
 }
 
 // s_waitcnt on this wave's vector-memory counter only (vmcnt(0)).
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
-
-// Workgroup barrier that waits for this wave's LDS operations only.
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // lgkmcnt(0)
-    __builtin_amdgcn_s_barrier();
-}
+__device__ __forceinline__ void wait_vm0() { wait_vmcnt<0>(); }
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint16_t *__restrict__ Qt,

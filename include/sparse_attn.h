@@ -7,9 +7,9 @@
  * every head h carries its own binary mask M_h over pairs of tiles: query
  * tile i attends to key tile j only when M_h[i, j] is set (Compact Attention
  * page, abstract: head-specific masks in one tile-aligned family; Fig. 1
- * caption: retained query-key regions; Fig. 3 caption: online inference loads
- * precomputed masks into block-sparse attention kernels and reuses each one
- * over an interval of adjacent denoising steps).  Inside the kept set the
+ * caption: retained query-key regions; Fig. 3 caption: masks are found
+ * offline, then compiled once and reused by the block-sparse kernels for
+ * several denoising steps in a row).  Inside the kept set the
  * result is exact softmax attention over the original keys and values (SCOPE
  * review page, abstract), with scores scaled by 1/sqrt(head_dim) by default:
  *

@@ -109,6 +109,14 @@ def _ranks_before(c1, c2):
     return (g1, m1) < (g2, m2)
 
 
+def _within_cost_bound(dw, dc, w_total, c_total, lam):
+    """The cost constraint: the recall a move loses, dw / w_total, is at most
+    lam times the cost fraction it saves, dc / c_total (lam = inf: always)."""
+    if math.isinf(lam):
+        return True
+    return float(dw) * float(c_total) <= lam * float(dc) * float(w_total)
+
+
 def search_head(grid, tile, counts, A_h, groups_h, tau, lam):
     """Returns ([(y, X, Y, x) per group], recall, cost)."""
     _, _, _, (nt, ny, nx) = _tile_coords(grid, tile)
@@ -128,8 +136,7 @@ def search_head(grid, tile, counts, A_h, groups_h, tau, lam):
                 dw, dc = int(mw[gone].sum()), int(mc[gone].sum())
                 if kept_w - dw < need:
                     continue
-                if not math.isinf(lam) and not (float(dw) * float(c_total) <=
-                                                 lam * float(dc) * float(w_total)):
+                if not _within_cost_bound(dw, dc, w_total, c_total, lam):
                     continue
                 cand = (dw, dc, g, m)
                 if best is None or _ranks_before(cand, best[0]):

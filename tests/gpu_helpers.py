@@ -59,13 +59,16 @@ def lse_bound(q_rows, k_max_norm, n_kept, d, scale, dtype, lse_ref):
     - The row sum adds n_kept positive fp32 terms: relative error
       <= n_kept 2^-24, i.e. that much in LSE.
     - On the bf16 path each probability is rounded to bf16 before it is
-      summed (relative 2^-9), the same rounded values that weight V.
+      summed: round-to-nearest to an 8-bit significand moves each term by
+      at most 2^-8 of itself, so the sum (all terms positive) moves by at
+      most 2^-8 of itself and LSE = ln(sum) by at most ln(1 + 2^-8) < 2^-8.
+      The same rounded values weight V.
     - exp2/log2 and the final scaling: a few ulp of max(1, |LSE|)."""
     u = 2.0 ** -24
     qn = np.linalg.norm(q_rows, axis=-1)
     t = d * u * scale * qn * k_max_norm + n_kept * u + 8 * u * np.maximum(1.0, np.abs(lse_ref))
     if dtype == "bf16":
-        t = t + 2.0 ** -9
+        t = t + 2.0 ** -8
     return t + 1e-7
 
 

@@ -223,3 +223,22 @@ def test_status_strings(sa):
     assert "mask" in sa.sparse_attn_status_string(sa.SPARSE_ATTN_NO_MASK)
     assert "Hilbert" in sa.sparse_attn_status_string(sa.SPARSE_ATTN_NO_ORDER)
     assert sa.sparse_attn_status_string(99) == "unknown status"
+
+
+def test_binding_refuses_mis_sized_host_arrays(sa):
+    """Host arrays the C side reads or writes per head are checked against
+    the handle before the call (no device needed: the checks come first)."""
+    h = sa.sparse_attn_create(3, 128, (2, 16, 32), (1, 8, 16), "bf16")
+    nT = sa.sparse_attn_layout(h)["tiles"]
+    mass = np.zeros((3, nT, nT), np.float32)
+    groups = np.array([(0, 0, 0, 0, 0, 0)] * 3, np.int32)
+    with pytest.raises(ValueError):  # groups_per_head for 2 of 3 heads
+        sa.sparse_attn_search_windows(h, mass, groups[:2], np.ones(2, np.int32), 0.9)
+    with pytest.raises(ValueError):  # rows != sum(groups_per_head)
+        sa.sparse_attn_search_windows(h, mass, groups[:2], np.ones(3, np.int32), 0.9)
+    with pytest.raises(ValueError):  # mass of 2 heads
+        sa.sparse_attn_search_windows(h, mass[:2], groups, np.ones(3, np.int32), 0.9)
+    with pytest.raises(ValueError):
+        sa.sparse_attn_set_mask(h, None, groups=groups, groups_per_head=np.ones(4, np.int32))
+    with pytest.raises(ValueError):
+        sa.sparse_attn_select_topk(h, [1, 2], None, None)

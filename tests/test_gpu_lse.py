@@ -185,10 +185,15 @@ def test_lse_argument_checks():
     o = torch.empty_like(q)
     ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
     buf = torch.empty(c.heads * c.N + 4, dtype=torch.float32, device="cuda")
-    for bad in (buf[1:1 + c.heads * c.N], q):  # misaligned; overlapping q
+    # misaligned; overlapping q (a raw pointer: the binding's size check
+    # would refuse q's 2-byte elements before the library sees it)
+    for bad in (buf[1:1 + c.heads * c.N], q.data_ptr()):
         with pytest.raises(sa.SparseAttnError) as e:
             sa.sparse_attn_forward_lse(h, q, k, v, o, bad, ws)
         assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    for bad in (buf, buf[:c.heads * c.N - 1], q):  # too long; too short; wrong element size
+        with pytest.raises(ValueError):
+            sa.sparse_attn_forward_lse(h, q, k, v, o, bad, ws)
     with pytest.raises(sa.SparseAttnError) as e:
         sa.sparse_attn_attend_raster(h, q, o, ws, lse=buf[1:1 + c.heads * c.N])
     assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG

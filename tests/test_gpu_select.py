@@ -3,8 +3,9 @@ oracle's selection.
 
 The GPU scores in fp32, the oracle in fp64, so a row whose k-th and
 (k+1)-th best scores are closer than fp32 rounding may keep a different
-tile; every differing tile must be such a near-tie, and every row keeps
-exactly k tiles."""
+tile; every differing tile must be such a near-tie, within a bound derived
+from the fp32 arithmetic (score_error_bound), every row keeps exactly k
+tiles, and near-tie differences stay rare (at most 1 per 100 rows)."""
 
 import numpy as np
 import pytest
@@ -37,6 +38,38 @@ def _scores(grid, tile, q, k, d):
                      for h in range(q.shape[0])]) / np.sqrt(d)
 
 
+def _abs(x):
+    """|x| with the dtype kept (bf16 bit patterns: clear the sign bit)."""
+    return x & np.uint16(0x7FFF) if x.dtype == np.uint16 else np.abs(x)
+
+
+def score_error_bound(grid, tile, q, k, d):
+    """Per tile pair, a bound on |S_gpu - S_exact| for the fp32 scores
+    s qbar_i . kbar_j, from the selection kernels' arithmetic (u = 2^-24,
+    first order in u):
+    - pool: a thread adds every RP-th row of a tile (RP = 2048 / d rows in
+      flight), then one thread adds the RP partial sums and divides by c,
+      so each feature mean passes through at most n = ceil(c / RP) - 1 +
+      RP - 1 additions and one division: |dqbar| <= n' u mean|x| with
+      n' = n + 1;
+    - score: d sequential fp32 FMAs and the scale multiply, at most
+      (d + 1) u s sum |qbar| |kbar|.
+    With a_i = mean |q| over tile i and b_j = mean |k| over tile j
+    (|qbar| <= a, |kbar| <= b):
+        |dS_ij| <= s u (n'_i + n'_j + d + 1) sum_f a_i[f] b_j[f]."""
+    u = 2.0 ** -24
+    s = 1.0 / np.sqrt(d)
+    rp = 2048 // d
+    c = oracle.tile_counts(grid, tile).astype(np.int64)
+    n1 = (-(-c // rp) - 1) + (rp - 1) + 1
+    out = []
+    for h in range(q.shape[0]):
+        a = oracle.tile_means(grid, tile, _abs(q[h]))
+        b = oracle.tile_means(grid, tile, _abs(k[h]))
+        out.append(s * u * (n1[:, None] + n1[None, :] + d + 1) * (a @ b.T) * (1 + 1e-6))
+    return np.stack(out)
+
+
 def _check(grid, tile, q, k, kh, dtype):
     heads, _, d = q.shape
     h = sa.sparse_attn_create(heads, d, grid, tile, dtype)
@@ -48,12 +81,21 @@ def _check(grid, tile, q, k, kh, dtype):
     diff = np.argwhere(got != want)
     if len(diff):
         S = _scores(grid, tile, q, k, d)
+        E = score_error_bound(grid, tile, q, k, d)
         for hh, i, j in diff:
+            # j sits on the wrong side of the k-th best exact score thr only if
+            # some pair j, j' straddling thr swapped order: |S_ij - thr| <=
+            # |S_ij - S_ij'| <= E_ij + E_ij' <= 2 max_j' E_ij'.
             row = np.sort(S[hh, i])[::-1]
             kk = kh[hh]
             thr = row[kk - 1]
-            tol = 1e-5 * max(1.0, abs(thr))
-            assert abs(S[hh, i, j] - thr) <= tol, (hh, i, j, S[hh, i, j], thr)
+            tol = 2 * E[hh, i].max()
+            assert abs(S[hh, i, j] - thr) <= tol, (hh, i, j, S[hh, i, j], thr, tol)
+    rows = heads * want.shape[1]
+    rows_diff = len({(hh, i) for hh, i, _ in diff})
+    print(f"  tiles differing from the oracle (near-ties): {len(diff)} in {rows_diff} of {rows} rows",
+          flush=True)
+    assert rows_diff <= max(1, rows // 100), (rows_diff, rows)
     return len(diff)
 
 
@@ -61,8 +103,7 @@ def test_hunyuan_masks_match_the_oracle():
     wl = make_workload("hunyuan", heads=6)
     kh = wl.info["k_per_head"]
     print(f"select hunyuan heads=6 k={kh}", flush=True)
-    n = _check(wl.grid, wl.tile, wl.q, wl.k, kh, "bf16")
-    print(f"  tiles differing from the oracle (near-ties): {n}", flush=True)
+    _check(wl.grid, wl.tile, wl.q, wl.k, kh, "bf16")
 
 
 @pytest.mark.parametrize("grid,tile,d,dtype", [

@@ -99,3 +99,25 @@ def test_argument_checks():
     with pytest.raises(sa.SparseAttnError) as e:
         sa.sparse_attn_search_windows(h, A, bad, [2], 0.5)
     assert e.value.status == sa.SPARSE_ATTN_BAD_MASK
+
+
+def test_library_reproduces_the_hand_worked_cases():
+    """The hand-derived cases of tests/golden/search_cases.json through the
+    library's search (their masses are exact in fp32)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "search_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        grid, tile = case["grid"], case["tile"]
+        a, b, e, _ = search._tile_coords(grid, tile)
+        n = np.asarray(case["n"], dtype=np.float64)
+        A = n[np.abs(a[:, None] - a[None, :]), np.abs(b[:, None] - b[None, :]),
+              np.abs(e[:, None] - e[None, :])] / case["den"]
+        lam = math.inf if case["lam"] == "inf" else float(case["lam"])
+        g_in, gph = _groups([tuple(g) for g in case["groups"]], 1)
+        h = sa.sparse_attn_create(1, 128, grid, tile, "bf16")
+        got, rec, cost = sa.sparse_attn_search_windows(h, A[None].astype(np.float32), g_in, gph,
+                                                       case["tau"], lam)
+        assert got.tolist() == case["expected_rows"], case["name"]
+        assert rec[0] == case["expected_recall"] and cost[0] == case["expected_cost"], case["name"]
