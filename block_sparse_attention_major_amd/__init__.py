@@ -51,7 +51,7 @@ SPARSE_ATTN_MAX_GROUPS = 8
 EXPORTED = [
     "sparse_attn_create", "sparse_attn_destroy", "sparse_attn_layout", "sparse_attn_mask_bytes",
     "sparse_attn_workspace_bytes", "sparse_attn_order_bytes", "sparse_attn_set_order",
-    "sparse_attn_set_mask", "sparse_attn_forward",
+    "sparse_attn_set_mask", "sparse_attn_forward", "sparse_attn_forward_noalloc",
     "sparse_attn_forward_lse", "sparse_attn_permute_kv", "sparse_attn_attend_raster",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
@@ -102,6 +102,7 @@ _sigs = {
     "sparse_attn_set_order": ([_vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_set_mask": ([_vp, _P(sparse_attn_mask), _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_forward": ([_vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "sparse_attn_forward_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_forward_lse": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_permute_kv": ([_vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "sparse_attn_attend_raster": ([_vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -327,6 +328,18 @@ def _lse(h, t):
 def sparse_attn_forward(h, q, k, v, o, ws, stream=None):
     _check(_lib.sparse_attn_forward(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _io(h, v, "v"), _io(h, o, "o"),
                                     _dptr(ws, "ws"), _nbytes(ws), _stream(stream)), h)
+
+
+SPARSE_ATTN_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def sparse_attn_forward_noalloc(h, q, k, v, o, stream=None):
+    """Forward without a workspace: the permuted K and V use the library's
+    fixed per-device scratch array (at most SPARSE_ATTN_NOALLOC_SCRATCH_BYTES;
+    larger layouts fail with UNSUPPORTED).  Calls overlapping in time on one
+    device race on that array."""
+    _check(_lib.sparse_attn_forward_noalloc(h.ptr, _io(h, q, "q"), _io(h, k, "k"), _io(h, v, "v"),
+                                            _io(h, o, "o"), _stream(stream)), h)
 
 
 def sparse_attn_forward_lse(h, q, k, v, o, lse, ws, stream=None):

@@ -5,6 +5,7 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -254,15 +255,15 @@ std::vector<int32_t> hilbert_sequence(int T, int H, int W, int k)
     return seq;
 }
 
-sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
+// Attention parameters over permuted K and V at kbuf and vbuf; q and o are
+// left for the caller to set.
+sa::AttnParams attn_params_kv(const sparse_attn_handle *h, const void *kbuf, const void *vbuf)
 {
-    const WsLayout w = ws_layout(h);
-    char *b = static_cast<char *>(ws);
     sa::AttnParams p;
-    p.q = b + w.q;
-    p.k = b + w.k;
-    p.v = b + w.v;
-    p.o = b + w.o;
+    p.q = nullptr;
+    p.k = kbuf;
+    p.v = vbuf;
+    p.o = nullptr;
     p.raster = 0;
     p.lse = nullptr;
     p.rows = sa::ListSet{h->mb.row_ptr, h->mb.cols, h->mb.order, h->mb.cap};
@@ -277,6 +278,17 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
     return p;
 }
 
+// Attention parameters over the four regions of a forward workspace.
+sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
+{
+    const WsLayout w = ws_layout(h);
+    char *b = static_cast<char *>(ws);
+    sa::AttnParams p = attn_params_kv(h, b + w.k, b + w.v);
+    p.q = b + w.q;
+    p.o = b + w.o;
+    return p;
+}
+
 hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p, hipStream_t s)
 {
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
@@ -286,6 +298,44 @@ hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p
 }
 
 size_t lse_bytes(const sparse_attn_handle *h) { return size_t(h->L.heads) * h->L.N * sizeof(float); }
+
+// Scratch of sparse_attn_forward_noalloc: the permuted K and V live in this
+// file-scope device array instead of a caller workspace.  Each device that
+// runs the library holds its own copy until the process ends.  In host code
+// `scratch` only names the symbol; its device address (per device) comes from
+// hipGetSymbolAddress and is the only thing passed to kernels.
+constexpr size_t kScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch_ptr[kMaxDevices] = {};
+
+// Bytes of scratch the no-allocation forward needs: K then V, each region
+// 256-byte aligned, as in the workspace.
+size_t scratch_need(const sparse_attn_handle *h) { return 2 * ws_layout(h).k; }
+
+// The current device's scratch address, looked up once per device.
+int scratch_address(sparse_attn_handle *h, char **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_fail(h, e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return SPARSE_ATTN_OK;
+}
 
 }  // namespace
 
@@ -733,6 +783,51 @@ int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, con
                         void *ws, size_t ws_bytes, void *stream)
 {
     return sparse_attn_forward_lse(h, q, k, v, o, nullptr, ws, ws_bytes, stream);
+}
+
+int sparse_attn_forward_noalloc(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
+                                void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_io(h, q, "q")) || (st = check_io(h, k, "k")) || (st = check_io(h, v, "v")) ||
+        (st = check_io(h, o, "o")))
+        return st;
+    const size_t need = scratch_need(h);
+    if (need > kScratchBytes)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED,
+                    "the permuted K and V need %zu bytes; the no-allocation forward holds at most %zu "
+                    "(use sparse_attn_forward with a workspace)",
+                    need, kScratchBytes);
+    if (!h->has_mask)
+        return fail(h, SPARSE_ATTN_NO_MASK, "set_mask must be called before forward");
+    const size_t n = io_bytes(h);
+    for (const void *p : {q, k, v})
+        if (overlaps(o, n, p, n))
+            return fail(h, SPARSE_ATTN_INVALID_ARG, "o must not overlap q, k or v");
+    char *kbuf = nullptr;
+    if ((st = scratch_address(h, &kbuf)))
+        return st;
+    // The workspace's K and V regions, carved from the scratch array.
+    const WsLayout w = ws_layout(h);
+    char *vbuf = kbuf + (w.v - w.k);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_permute_rows(h->L, h->elem_bytes, k, kbuf, s);
+    if (e == hipSuccess)
+        e = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? sa::launch_permute_tile_columns(h->L, v, vbuf, s)
+                                                      : sa::launch_permute_rows(h->L, h->elem_bytes, v, vbuf, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "permute launch");
+    sa::AttnParams p = attn_params_kv(h, kbuf, vbuf);
+    p.q = q;
+    p.o = o;
+    p.raster = 1;
+    p.lse = nullptr;
+    e = launch_attention(h, p, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "attention launch");
+    return SPARSE_ATTN_OK;
 }
 
 int sparse_attn_tile_mass(sparse_attn_handle *h, const void *q, const void *k, void *ws,

@@ -33,7 +33,9 @@
  *     finish before anything is enqueued, so a failed call leaves no GPU work
  *     behind.  sparse_attn_last_error() then describes the failure.
  *   - Device pointers are caller-owned HIP device memory (for example torch
- *     tensors), 16-byte aligned.  The library never allocates device memory.
+ *     tensors), 16-byte aligned.  The library never allocates device memory;
+ *     its only device memory of its own is the fixed scratch array of
+ *     sparse_attn_forward_noalloc, part of the loaded code object.
  *   - Host arrays a call takes (window specs, per-head k) are read or
  *     staged before the call returns; the caller may reuse them at once.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
@@ -268,6 +270,28 @@ int sparse_attn_forward(sparse_attn_handle *h, const void *q, const void *k, con
  */
 int sparse_attn_forward_lse(sparse_attn_handle *h, const void *q, const void *k, const void *v,
                             void *o, float *lse, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * sparse_attn_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation calls).  The permuted K and V go to a
+ * library-owned device array of fixed size (SPARSE_ATTN_NOALLOC_SCRATCH_BYTES,
+ * 128 MiB; each device that runs the library holds its own copy until the
+ * process ends) instead of ws; the call allocates nothing and calls no
+ * allocating routine.  The array's device address is looked up on the first
+ * call on each device (the device current at the call); the stream must
+ * belong to that device.  Same arguments, results and errors as
+ * sparse_attn_forward, plus UNSUPPORTED when the permuted K and V need more
+ * than the array holds (2 * heads * tiles * B * head_dim * element bytes,
+ * each half rounded up to 256 bytes); the scratch check comes before the
+ * mask check.  Every call on a device shares that device's array: calls
+ * that overlap in time on one device (other streams, other threads) race
+ * and must be ordered by the caller.  The array keeps the last call's
+ * contents; nothing in it needs to start at zero.
+ */
+#define SPARSE_ATTN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int sparse_attn_forward_noalloc(sparse_attn_handle *h, const void *q, const void *k, const void *v, void *o,
+                                void *stream);
 
 /* The two stages of sparse_attn_forward(_lse), callable one by one (same
  * arguments and errors): permute K and V into ws, then attention reading q

@@ -242,3 +242,23 @@ def test_binding_refuses_mis_sized_host_arrays(sa):
         sa.sparse_attn_set_mask(h, None, groups=groups, groups_per_head=np.ones(4, np.int32))
     with pytest.raises(ValueError):
         sa.sparse_attn_select_topk(h, [1, 2], None, None)
+
+
+def test_noalloc_forward_refuses_layouts_beyond_its_scratch(sa):
+    """The no-allocation forward holds at most 128 MiB of permuted K and V;
+    a larger layout is refused before anything touches the device (the
+    scratch check precedes the mask check)."""
+    h = sa.sparse_attn_create(40, 128, (21, 45, 80), (1, 8, 16), "bf16")  # 1.65 GB of K and V
+    L = sa.sparse_attn_layout(h)
+    assert 2 * L["ws_offset_k"] > sa.SPARSE_ATTN_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 40
+    n = 40 * L["tokens"] * 128 * 2
+    st = sa._lib.sparse_attn_forward_noalloc(h.ptr, fake, fake + n, fake + 2 * n, fake + 3 * n, None)
+    assert st == sa.SPARSE_ATTN_UNSUPPORTED
+    assert "no-allocation forward holds at most" in sa.sparse_attn_last_error(h)
+    small = sa.sparse_attn_create(12, 128, (8, 30, 40), (1, 8, 16), "bf16")  # 75.5 MB: fits
+    Ls = sa.sparse_attn_layout(small)
+    assert 2 * Ls["ws_offset_k"] <= sa.SPARSE_ATTN_NOALLOC_SCRATCH_BYTES
+    ns = 12 * Ls["tokens"] * 128 * 2
+    st = sa._lib.sparse_attn_forward_noalloc(small.ptr, fake, fake + ns, fake + 2 * ns, fake + 3 * ns, None)
+    assert st == sa.SPARSE_ATTN_NO_MASK
