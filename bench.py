@@ -96,10 +96,27 @@ def cpu_baseline(wl, M, budget_s=15.0):
     t0 = time.perf_counter()
     oracle.attention_rows(wl.grid, wl.tile, wl.q, wl.k, wl.v, M, rows, threads=threads)
     dt = time.perf_counter() - t0
+    F_full = wl.info["flops_alg"]
     return {"value": f / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} query rows drawn uniformly over all heads and tokens of the workload "
                       f"({f / 1e12:.3f} TFLOP algorithmic, {dt:.1f} s wall, fp64, OpenMP)",
-            "seconds": dt}
+            "seconds": dt,
+            "full_workload_s_extrapolated": F_full / (f / dt),
+            "full_workload_note": "the whole workload's oracle time, extrapolated from the sample's rate "
+                                  "by algorithmic FLOPs (not measured)"}
+
+
+def input_fingerprint(wl):
+    """Seed and short hashes of the workload's mask description and inputs,
+    so a bench record names exactly what it measured."""
+    def h(*arrays):
+        d = hashlib.blake2b(digest_size=8)
+        for a in arrays:
+            d.update(np.ascontiguousarray(a).view(np.uint8).reshape(-1))
+        return d.hexdigest()
+    mask = h(wl.bitmap) if wl.mask_kind == "bitmap" else h(wl.groups, wl.groups_per_head)
+    return {"seed": wl.config.seed, "mask_hash": mask, "qkv_hash": h(wl.q, wl.k, wl.v),
+            "hash": "blake2b-64 of the raw bytes"}
 
 
 def topk_order_comparison(sa, wl, q, k, v, density, stream):
@@ -419,7 +436,8 @@ def main():
                    "tile_density": round(info["tile_density"], 5),
                    "token_density": round(info["token_density"], 5),
                    "step": "mask compile + permute K, V + block-sparse attention (Q read and O "
-                           "written in raster order by the attention kernels)"},
+                           "written in raster order by the attention kernels)",
+                   "inputs": input_fingerprint(wl)},
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F,
