@@ -40,12 +40,12 @@ WORKLOAD_NAMES = {
     "long": "long-video stress: 40 heads x 151,200 tokens, d=128, tile 1x8x16, +-4 frame axial masks",
     "small": "small video: 12 heads x 9,600 tokens, d=128, tile 1x8x16, dual-window masks",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_wan_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_{}_traffic.json")  # per workload
 # The attention stage's two kernels, and the files that decide their work
 # split and layout; counter results taken on other versions of these are
 # not reported.
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_attention_major_amd", "csrc", f)
-                  for f in ("attn_mfma.hip", "attn_rows.hip", "mask.hip", "common.h")]
+                  for f in ("attn_mfma.hip", "attn_rows.hip", "mfma_util.h", "mask.hip", "common.h")]
 ATTN_KERNELS = "attn_mfma_kernel<128> (query-tile pairs) + attn_rows_kernel<128> (single tiles)"
 
 
@@ -61,7 +61,7 @@ def traffic_per_launch(workload):
     """HBM bytes per attention launch from committed counter runs, or None if
     they were taken on another version of the kernel or workload."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(TRAFFIC_FILE.format(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -279,18 +279,19 @@ def main():
     ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
     mask_buf = torch.empty(sa.sparse_attn_mask_bytes(h, info["nnz"]), dtype=torch.uint8, device="cuda")
     dense_buf = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
-    ones = t(ones_bitmap(wl))
+    u8 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).cuda()
+    ones = u8(ones_bitmap(wl))
     stream = torch.cuda.current_stream()
 
     def set_mask():
         if wl.mask_kind == "bitmap":
-            sa.sparse_attn_set_mask(h, mask_buf, bitmap=t(wl.bitmap), max_nnz=info["nnz"])
+            sa.sparse_attn_set_mask(h, mask_buf, bitmap=u8(wl.bitmap), max_nnz=info["nnz"])
         else:
             sa.sparse_attn_set_mask(h, mask_buf, groups=wl.groups, groups_per_head=wl.groups_per_head,
                                     max_nnz=info["nnz"])
 
     if wl.mask_kind == "bitmap":
-        bitmap_dev = t(wl.bitmap)
+        bitmap_dev = u8(wl.bitmap)
 
         def set_mask():  # noqa: F811  (bitmap already resident)
             sa.sparse_attn_set_mask(h, mask_buf, bitmap=bitmap_dev, max_nnz=info["nnz"])

@@ -37,6 +37,12 @@ SPARSE_ATTN_HIP_ERROR = 6
 SPARSE_ATTN_NO_ORDER = 7
 SPARSE_ATTN_ORDER_TILES = 0
 SPARSE_ATTN_ORDER_HILBERT = 1
+SPARSE_ATTN_PAIRING_AUTO = 0
+SPARSE_ATTN_PAIRING_OVERLAP = 1
+SPARSE_ATTN_PAIRING_ALL = 2
+SPARSE_ATTN_PAIRING_NONE = 3
+_PAIRINGS = {"auto": SPARSE_ATTN_PAIRING_AUTO, "overlap": SPARSE_ATTN_PAIRING_OVERLAP,
+             "all": SPARSE_ATTN_PAIRING_ALL, "none": SPARSE_ATTN_PAIRING_NONE}
 
 SPARSE_ATTN_F32 = 0
 SPARSE_ATTN_BF16 = 1
@@ -65,7 +71,7 @@ class sparse_attn_config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("grid", ctypes.c_int32 * 3), ("tile", ctypes.c_int32 * 3),
                 ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32)]
 
 
 class sparse_attn_window_group(ctypes.Structure):
@@ -87,7 +93,7 @@ class sparse_attn_layout_info(ctypes.Structure):
                 ("ws_offset_v", ctypes.c_size_t), ("ws_offset_o", ctypes.c_size_t),
                 ("ws_bytes", ctypes.c_size_t), ("pair_axis", ctypes.c_int32),
                 ("pair_grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int64),
-                ("order", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -239,16 +245,19 @@ def _nbytes(t):
 
 
 def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0,
-                       order=SPARSE_ATTN_ORDER_TILES):
+                       order=SPARSE_ATTN_ORDER_TILES, pairing=SPARSE_ATTN_PAIRING_AUTO):
     """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32; order:
-    "tiles"/"hilbert" or SPARSE_ATTN_ORDER_*."""
+    "tiles"/"hilbert" or SPARSE_ATTN_ORDER_*; pairing: "auto"/"overlap"/
+    "all"/"none" or SPARSE_ATTN_PAIRING_*."""
     if isinstance(dtype, str):
         dtype = {"bf16": SPARSE_ATTN_BF16, "f32": SPARSE_ATTN_F32}[dtype]
     if isinstance(order, str):
         order = {"tiles": SPARSE_ATTN_ORDER_TILES, "hilbert": SPARSE_ATTN_ORDER_HILBERT}[order]
+    if isinstance(pairing, str):
+        pairing = _PAIRINGS[pairing]
     cfg = sparse_attn_config(int(heads), int(head_dim), (ctypes.c_int32 * 3)(*grid),
                              (ctypes.c_int32 * 3)(*tile), int(dtype), float(softmax_scale),
-                             int(order))
+                             int(order), int(pairing))
     out = _vp()
     st = _lib.sparse_attn_create(ctypes.byref(cfg), ctypes.byref(out))
     if st != SPARSE_ATTN_OK:

@@ -199,6 +199,7 @@ struct MaskBuffers {
     int nchunks;
     int pair;       // 0: rows r = h nT + i; 1: pairs r = h nP + pr (entries carry keep bits)
     int *flag;      // pairs only, [R]: 1 = the pair kernel serves the pair (see kPairNum)
+    int pairing;    // pairs only: SPARSE_ATTN_PAIRING_OVERLAP, _ALL or _NONE (AUTO resolved)
     FastDiv dplane; // ny * nx: tiles per tile-grid plane
     FastDiv drow;   // nx: tiles per tile-grid row
 };
@@ -210,6 +211,14 @@ struct MaskBuffers {
 // go to the row kernel.  A pair with no kept tiles is served by the pair
 // kernel (it writes zeros).
 constexpr int kPairNum = 7, kPairDen = 10;
+
+// SPARSE_ATTN_PAIRING_AUTO: a layout with at most kAllPairsMax query-tile
+// pairs over all heads (a few per compute unit) sends every pair to the
+// pair kernel, whatever the overlap of its two lists: with so little work
+// the GPU is not filled, and the rows a separate row-kernel launch would
+// take (often the longest) would run after the pair kernel, on the critical
+// path.
+constexpr long long kAllPairsMax = 1024;
 
 constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
 

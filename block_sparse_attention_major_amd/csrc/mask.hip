@@ -171,7 +171,9 @@ __global__ __launch_bounds__(256) void count_kernel(Layout L, MaskBuffers mb,
         n12 += __shfl_xor(n12, off);
     }
     if (mb.pair) {
-        const int accept = (long long)n * kPairDen <= (long long)kPairNum * n12 ? 1 : 0;
+        const int accept = mb.pairing == SPARSE_ATTN_PAIRING_ALL    ? 1
+                           : mb.pairing == SPARSE_ATTN_PAIRING_NONE ? 0
+                           : (long long)n * kPairDen <= (long long)kPairNum * n12 ? 1 : 0;
         if (lane == 0)
             mb.flag[r] = accept;
         if (!accept)

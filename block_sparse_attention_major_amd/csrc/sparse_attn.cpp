@@ -293,11 +293,31 @@ hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p
 {
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
         return sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
-    hipError_t e = sa::launch_attention_mfma(h->L, p, s);
-    return e == hipSuccess ? sa::launch_attention_rows(h->L, p, s) : e;
+    // The pair kernel skips pairs it does not serve and the row kernel
+    // tiles the pair kernel serves; a pairing that gives one kernel nothing
+    // leaves its launch out.
+    const int pairing = h->pb.pairing;
+    hipError_t e = hipSuccess;
+    if (pairing != SPARSE_ATTN_PAIRING_NONE)
+        e = sa::launch_attention_mfma(h->L, p, s);
+    if (e == hipSuccess && pairing != SPARSE_ATTN_PAIRING_ALL)
+        e = sa::launch_attention_rows(h->L, p, s);
+    return e;
 }
 
 size_t lse_bytes(const sparse_attn_handle *h) { return size_t(h->L.heads) * h->L.N * sizeof(float); }
+
+// The pairing in effect on the matrix-core path (AUTO resolved); -1 for the
+// vector-ALU kernel.
+int pairing_of(const sparse_attn_handle *h)
+{
+    if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
+        return -1;
+    if (h->cfg.pairing != SPARSE_ATTN_PAIRING_AUTO)
+        return h->cfg.pairing;
+    return (long long)h->L.heads * h->L.nP <= sa::kAllPairsMax ? SPARSE_ATTN_PAIRING_ALL
+                                                              : SPARSE_ATTN_PAIRING_OVERLAP;
+}
 
 // Scratch of sparse_attn_forward_noalloc: the permuted K and V live in this
 // file-scope device array instead of a caller workspace.  Each device that
@@ -384,6 +404,8 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "tile volume %lld exceeds 128", B);
     if (c.order != SPARSE_ATTN_ORDER_TILES && c.order != SPARSE_ATTN_ORDER_HILBERT)
         return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "order must be TILES or HILBERT");
+    if (c.pairing < SPARSE_ATTN_PAIRING_AUTO || c.pairing > SPARSE_ATTN_PAIRING_NONE)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "pairing must be AUTO, OVERLAP, ALL or NONE");
     const long long N0 = (long long)c.grid[0] * c.grid[1] * c.grid[2];
     if (N0 >= (1ll << 31))
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED, "%lld tokens do not fit 32-bit token ids", N0);
@@ -487,6 +509,7 @@ int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *inf
         info->pair_grid[a] = h->L.pn[a];
     info->pairs = h->L.nP;
     info->order = h->cfg.order;
+    info->pairing = pairing_of(h);
     return SPARSE_ATTN_OK;
 }
 
@@ -606,6 +629,7 @@ int sparse_attn_set_mask(sparse_attn_handle *h, const sparse_attn_mask *m, void 
         pb.nchunks = ml.pnchunks;
         pb.pair = 1;
         pb.flag = reinterpret_cast<int *>(base + ml.p_flag);
+        pb.pairing = pairing_of(h);
     }
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -16,8 +16,9 @@ their structure on the host, without any reference implementation:
       two tiles' rows, each entry carrying the key tile, its real token count
       and which of the two tiles keeps it; a pair it does not serve (flag 0)
       is empty;
-    - the flag follows the sharing rule: served when the union is at most
-      7/10 of the two rows' total length (an empty pair is served);
+    - the flag follows the layout's pairing: under OVERLAP a pair is served
+      when the union is at most 7/10 of the two rows' total length (an empty
+      pair is served), under ALL always, under NONE never;
     - the pair work order is sorted like the row order.
 
 It raises ValueError naming the first violation and returns a small summary
@@ -27,7 +28,8 @@ use it in tests and debugging, not in a timed loop.
 
 import numpy as np
 
-from . import (SPARSE_ATTN_KERNEL_MFMA_BF16, SPARSE_ATTN_ORDER_HILBERT, sparse_attn_layout,
+from . import (SPARSE_ATTN_KERNEL_MFMA_BF16, SPARSE_ATTN_ORDER_HILBERT, SPARSE_ATTN_PAIRING_ALL,
+               SPARSE_ATTN_PAIRING_NONE, sparse_attn_layout,
                sparse_attn_mask_info, sparse_attn_read_index_lists, sparse_attn_read_pair_lists)
 
 PAIR_NUM, PAIR_DEN = 7, 10
@@ -113,7 +115,12 @@ def check_pair_lists(rows, prp, pcl, pod, pfl, L, counts, heads):
         r1 = rows[hh * nT + t1]
         r2 = rows[hh * nT + t2] if t2 >= 0 else np.zeros(0, np.int64)
         union = np.union1d(r1, r2)
-        accept = union.size * PAIR_DEN <= PAIR_NUM * (r1.size + r2.size)
+        if L["pairing"] == SPARSE_ATTN_PAIRING_ALL:
+            accept = True
+        elif L["pairing"] == SPARSE_ATTN_PAIRING_NONE:
+            accept = False
+        else:
+            accept = union.size * PAIR_DEN <= PAIR_NUM * (r1.size + r2.size)
         if pfl[p] != int(accept):
             raise ValueError(f"pair {p}: flag {pfl[p]}, the sharing rule gives {int(accept)}")
         seg = pcl[prp[p]:prp[p + 1]]

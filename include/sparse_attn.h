@@ -114,6 +114,30 @@ enum { SPARSE_ATTN_ORDER_TILES = 0, SPARSE_ATTN_ORDER_HILBERT = 1 };
 /* Maximum temporal-distance groups per head in a dual-window mask. */
 #define SPARSE_ATTN_MAX_GROUPS 8
 
+/*
+ * How the matrix-core path splits query tiles between its two kernels
+ * (sparse_attn_config.pairing).  The pair kernel runs two neighbouring query
+ * tiles per workgroup over the union of their key lists; the row kernel runs
+ * one query tile per workgroup.  This is the library's own work split (the
+ * pages define only the per-tile mask); results are the same either way.
+ *   AUTO    (0): ALL when the layout has at most 1024 pairs over all heads
+ *                (too little work to fill the GPU, and a second launch for
+ *                single tiles would put their rows on the critical path),
+ *                otherwise OVERLAP.
+ *   OVERLAP (1): a pair goes to the pair kernel when the union of its two
+ *                lists is at most 7/10 of their total length (and when both
+ *                are empty); its tiles go to the row kernel otherwise.
+ *   ALL     (2): every pair goes to the pair kernel; no row-kernel launch.
+ *   NONE    (3): every tile goes to the row kernel; no pair-kernel launch.
+ * The vector-ALU kernel ignores it.
+ */
+enum {
+    SPARSE_ATTN_PAIRING_AUTO = 0,
+    SPARSE_ATTN_PAIRING_OVERLAP = 1,
+    SPARSE_ATTN_PAIRING_ALL = 2,
+    SPARSE_ATTN_PAIRING_NONE = 3
+};
+
 typedef struct sparse_attn_config {
     int32_t heads;         /* >= 1 */
     int32_t head_dim;      /* 64 or 128 */
@@ -122,6 +146,7 @@ typedef struct sparse_attn_config {
     int32_t dtype;         /* SPARSE_ATTN_F32 or SPARSE_ATTN_BF16 */
     float softmax_scale;   /* score scale s; 0 selects 1 / sqrt(head_dim) */
     int32_t order;         /* SPARSE_ATTN_ORDER_TILES (0) or SPARSE_ATTN_ORDER_HILBERT */
+    int32_t pairing;       /* SPARSE_ATTN_PAIRING_* (0 = AUTO) */
 } sparse_attn_config;
 
 /*
@@ -174,6 +199,9 @@ typedef struct sparse_attn_layout_info {
     int32_t pair_grid[3];
     int64_t pairs;
     int32_t order;         /* SPARSE_ATTN_ORDER_* of the handle */
+    /* The pairing in effect (OVERLAP, ALL or NONE; AUTO resolved), or -1
+     * for the vector-ALU kernel. */
+    int32_t pairing;
 } sparse_attn_layout_info;
 
 typedef struct sparse_attn_handle sparse_attn_handle;
@@ -184,7 +212,7 @@ typedef struct sparse_attn_handle sparse_attn_handle;
  * tiles at the far edges of a grid the tile does not divide are clipped.
  * Each tile owns B consecutive slots: its c real tokens fill the first c in
  * raster order over the clipped tile, the rest are empty.
- * Errors: INVALID_ARG (null, non-positive sizes, bad dtype or order),
+ * Errors: INVALID_ARG (null, non-positive sizes, bad dtype, order or pairing),
  * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31,
  * N >= 2^31, a Hilbert grid side above 2^21).
  * On success *out owns host memory only; release it with sparse_attn_destroy.

@@ -28,16 +28,19 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_is_tied_to_the_profiled_sources(tmp_path):
     b = _bench_module()
-    with open(b.TRAFFIC_FILE) as f:
+    with open(b.TRAFFIC_FILE.format("wan")) as f:
         t = json.load(f)
     assert t["workload"] == "wan" and len(t["kernel_source_sha256_16"]) == 16
     # A profile taken on other sources, or for another workload, gives no figure.
     stale = dict(t, kernel_source_sha256_16="0" * 16)
-    p = tmp_path / "traffic.json"
-    p.write_text(json.dumps(stale))
-    b.TRAFFIC_FILE = str(p)
+    (tmp_path / "stale").mkdir()
+    (tmp_path / "stale" / "wan.json").write_text(json.dumps(stale))
+    b.TRAFFIC_FILE = str(tmp_path / "stale" / "{}.json")
     assert b.traffic_per_launch("wan") is None
-    p.write_text(json.dumps(t))
+    (tmp_path / "good").mkdir()
+    (tmp_path / "good" / "wan.json").write_text(json.dumps(t))
+    (tmp_path / "good" / "hunyuan.json").write_text(json.dumps(t))  # names the wrong workload
+    b.TRAFFIC_FILE = str(tmp_path / "good" / "{}.json")
     want = b.traffic_per_launch("wan") if t["kernel_source_sha256_16"] == b.kernel_source_hash() else None
     assert b.traffic_per_launch("hunyuan") is None
     if want is not None:

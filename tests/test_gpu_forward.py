@@ -22,9 +22,11 @@ pytestmark = pytest.mark.gpu
 class Case:
     """Inputs of one forward: grid, tile, q/k/v (numpy), mask."""
 
-    def __init__(self, grid, tile, q, k, v, dtype, bitmap=None, groups=None, gph=None, scale=0.0):
+    def __init__(self, grid, tile, q, k, v, dtype, bitmap=None, groups=None, gph=None, scale=0.0,
+                 pairing="auto"):
         self.grid, self.tile, self.q, self.k, self.v = grid, tile, q, k, v
         self.dtype, self.bitmap, self.groups, self.gph, self.scale = dtype, bitmap, groups, gph, scale
+        self.pairing = pairing
         self.heads, self.N, self.d = q.shape
 
     @staticmethod
@@ -45,7 +47,7 @@ class Case:
 
 
 def gpu_forward(c, stages=False):
-    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale)
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing)
     mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
     if c.bitmap is not None:
         sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.bitmap))
@@ -78,10 +80,17 @@ def test_tiny_fp32():
     assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
 
 
-def test_small_bf16():
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_small_bf16(pairing):
+    """The Small workload through each work split of the matrix-core path
+    (auto sends every pair to the pair kernel at this size; overlap splits
+    pairs and single tiles; none runs the row kernel only)."""
     wl = make_workload("small")
-    _, _, layout = full_check(Case.of(wl), "small")
+    c = Case.of(wl)
+    c.pairing = pairing
+    got, _, layout = full_check(c, f"small pairing={pairing}")
     assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16
+    assert layout["pairing"] == (sa.SPARSE_ATTN_PAIRING_ALL if pairing == "auto" else sa._PAIRINGS[pairing])
 
 
 def test_small_dense_mask():
@@ -115,9 +124,11 @@ def _random_case(grid, tile, d, dtype, heads=3, p=0.4, seed=0, empty_row=True, s
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
     ((2, 5, 7), (2, 2, 3), 64, "f32"),
 ])
-def test_ragged_shapes_with_empty_rows(grid, tile, d, dtype):
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_ragged_shapes_with_empty_rows(grid, tile, d, dtype, pairing):
     c = _random_case(grid, tile, d, dtype)
-    got, want, _ = full_check(c, "ragged")
+    c.pairing = pairing
+    got, want, _ = full_check(c, f"ragged pairing={pairing}")
     nT = oracle.num_tiles(grid, tile)
     # the empty row (head 0, query tile nT // 2) outputs exactly zero
     perm, _ = oracle.perm(grid, tile)

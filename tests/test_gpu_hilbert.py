@@ -25,8 +25,8 @@ def _rand(shape, seed, dtype):
     return x if dtype == "f32" else f32_to_bf16_bits(x)
 
 
-def _handle(heads, d, grid, tile, dtype):
-    h = sa.sparse_attn_create(heads, d, grid, tile, dtype, order="hilbert")
+def _handle(heads, d, grid, tile, dtype, pairing="auto"):
+    h = sa.sparse_attn_create(heads, d, grid, tile, dtype, order="hilbert", pairing=pairing)
     buf = torch.empty(sa.sparse_attn_order_bytes(h), dtype=torch.uint8, device="cuda")
     sa.sparse_attn_set_order(h, buf)
     h.order_buf = buf  # keep it alive with the handle
@@ -110,7 +110,8 @@ def _forward(h, q, k, v, M, lse=True, stages=False):
     ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # B = 32: vector-ALU kernel
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
 ])
-def test_forward_and_lse_match_the_oracle(grid, tile, d, dtype):
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_forward_and_lse_match_the_oracle(grid, tile, d, dtype, pairing):
     heads = 3
     N = int(np.prod(grid))
     seq, g1, t1 = _seq_view(grid, tile)
@@ -118,8 +119,8 @@ def test_forward_and_lse_match_the_oracle(grid, tile, d, dtype):
     q, k, v = (_rand((heads, N, d), s, dtype) for s in (11, 12, 13))
     M = (np.random.default_rng(14).random((heads, nT, nT)) < 0.35).astype(np.uint8)
     M[1, nT // 2] = 0
-    print(f"hilbert forward grid={grid} tile={tile} d={d} {dtype}", flush=True)
-    h = _handle(heads, d, grid, tile, dtype)
+    print(f"hilbert forward grid={grid} tile={tile} d={d} {dtype} pairing={pairing}", flush=True)
+    h = _handle(heads, d, grid, tile, dtype, pairing)
     o, lse = _forward(h, q, k, v, M)
     staged, _ = _forward(h, q, k, v, M, stages=True)
     assert np.array_equal(o, staged)

@@ -26,9 +26,9 @@ def _rand(shape, seed, dtype):
 
 
 class Inputs:
-    def __init__(self, grid, tile, q, k, v, dtype, M, scale=0.0):
+    def __init__(self, grid, tile, q, k, v, dtype, M, scale=0.0, pairing="auto"):
         self.grid, self.tile, self.q, self.k, self.v = grid, tile, q, k, v
-        self.dtype, self.M, self.scale = dtype, M, scale
+        self.dtype, self.M, self.scale, self.pairing = dtype, M, scale, pairing
         self.heads, self.N, self.d = q.shape
 
     def oracle_scale(self):
@@ -46,7 +46,7 @@ def _random_inputs(grid, tile, d, dtype, heads=3, p=0.4, seed=0):
 
 def _gpu(c, mode):
     """o (numpy, input dtype) and lse (numpy fp32 or None) of one path."""
-    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale)
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing)
     mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
     sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.M))
     q, k, v = dev(c.q), dev(c.k), dev(c.v)
@@ -106,9 +106,11 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
-def test_fused_forward_equals_three_stages(grid, tile, d, dtype):
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_fused_forward_equals_three_stages(grid, tile, d, dtype, pairing):
     c = _random_inputs(grid, tile, d, dtype)
-    print(f"fused vs stages grid={grid} tile={tile} d={d} {dtype}", flush=True)
+    c.pairing = pairing
+    print(f"fused vs stages grid={grid} tile={tile} d={d} {dtype} pairing={pairing}", flush=True)
     fused, _ = _gpu(c, "forward")
     staged, _ = _gpu(c, "stages")
     with_lse, _ = _gpu(c, "forward_lse")
@@ -119,9 +121,11 @@ def test_fused_forward_equals_three_stages(grid, tile, d, dtype):
 
 
 @pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
-def test_lse_matches_the_oracle(grid, tile, d, dtype):
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_lse_matches_the_oracle(grid, tile, d, dtype, pairing):
     c = _random_inputs(grid, tile, d, dtype)
-    print(f"lse grid={grid} tile={tile} d={d} {dtype}", flush=True)
+    c.pairing = pairing
+    print(f"lse grid={grid} tile={tile} d={d} {dtype} pairing={pairing}", flush=True)
     o, lse = _gpu(c, "forward_lse")
     _check_lse(c, lse, "ragged")
     want = oracle.attention(c.grid, c.tile, c.q, c.k, c.v, c.M, scale=c.oracle_scale())
@@ -152,14 +156,15 @@ def test_lse_all_rows_empty():
     assert np.all(as_f64(o) == 0.0)
 
 
-def test_lse_full_size_wan_sampled():
-    """The Wan-shaped workload at full size, in the bench's launch
-    configuration; LSE of sampled queries (every head: the first, last and
-    a clipped query tile, plus random tokens) against the oracle."""
-    wl = make_workload("wan")
+@pytest.mark.parametrize("name", ["wan", "hunyuan", "long"])
+def test_lse_full_size_sampled(name):
+    """The 720p workloads at full size, in the bench's launch configuration;
+    LSE of sampled queries (every head: the first, last and a clipped query
+    tile, the head's longest row, plus random tokens) against the oracle."""
+    wl = make_workload(name)
     M = oracle.mask_of(wl)
     c = Inputs(wl.grid, wl.tile, wl.q, wl.k, wl.v, wl.dtype, M)
-    print(f"lse wan full heads={c.heads}", flush=True)
+    print(f"lse {name} full heads={c.heads}", flush=True)
     _, lse = _gpu(c, "forward_lse")
     rng = np.random.default_rng(3)
     B = int(np.prod(wl.tile))
@@ -168,11 +173,12 @@ def test_lse_full_size_wan_sampled():
     clipped = int(np.nonzero(counts < B)[0][0])
     rows = []
     for h in range(c.heads):
-        for t in (0, clipped, len(counts) - 1):
+        longest = int(np.argmax(M[h].sum(axis=1)))
+        for t in sorted({0, clipped, len(counts) - 1, longest}):
             toks = perm[t * B:t * B + counts[t]]
             rows += (h * c.N + rng.choice(toks, size=4, replace=False)).tolist()
         rows += (h * c.N + rng.choice(c.N, size=8, replace=False)).tolist()
-    _check_lse(c, lse, "wan sampled", rows=np.array(rows, dtype=np.int64))
+    _check_lse(c, lse, f"{name} sampled", rows=np.array(rows, dtype=np.int64))
     assert np.all(np.isfinite(lse[:, ::991]))
 
 

@@ -6,8 +6,10 @@ work split (the pages define only the per-tile mask); the expected lists are
 derived from the oracle's mask and tile sizes alone, by the rule the header
 documents: tiles (2c, 2c + 1) along the pair axis form pair c; the list of a
 pair the pair kernel serves is the ascending union of its tiles' rows, each
-entry j | c_j << 16 | keep bits << 24; a pair is served when 10 |union| <=
-7 (|row 1| + |row 2|), otherwise its list is empty; the work order sorts
+entry j | c_j << 16 | keep bits << 24; under the OVERLAP pairing a pair is
+served when 10 |union| <= 7 (|row 1| + |row 2|), under ALL always, under
+NONE never (AUTO: ALL for layouts of at most 1024 pairs over all heads,
+else OVERLAP); a pair not served has an empty list; the work order sorts
 pairs by decreasing list length, ties by pair id."""
 
 import numpy as np
@@ -46,10 +48,13 @@ def _tile_pairs(L):
     return out
 
 
-def _expected(M, L, counts):
+def _expected(M, L, counts, mode):
     heads, nT, _ = M.shape
     pairs = _tile_pairs(L)
     P = len(pairs)
+    want_pairing = mode if mode != sa.SPARSE_ATTN_PAIRING_AUTO else (
+        sa.SPARSE_ATTN_PAIRING_ALL if heads * P <= 1024 else sa.SPARSE_ATTN_PAIRING_OVERLAP)
+    assert L["pairing"] == want_pairing
     lens, flags, lists = [], [], []
     for h in range(heads):
         for t1, t2 in pairs:
@@ -57,7 +62,12 @@ def _expected(M, L, counts):
             k2 = M[h, t2].astype(bool) if t2 >= 0 else np.zeros(nT, bool)
             bits = k1.astype(np.int64) | (k2.astype(np.int64) << 1)
             j = np.nonzero(bits)[0]
-            served = 10 * len(j) <= 7 * (int(k1.sum()) + int(k2.sum()))
+            if want_pairing == sa.SPARSE_ATTN_PAIRING_ALL:
+                served = True
+            elif want_pairing == sa.SPARSE_ATTN_PAIRING_NONE:
+                served = False
+            else:
+                served = 10 * len(j) <= 7 * (int(k1.sum()) + int(k2.sum()))
             flags.append(int(served))
             if served:
                 lists.append(j | (counts[j].astype(np.int64) << 16) | (bits[j] << 24))
@@ -72,10 +82,10 @@ def _expected(M, L, counts):
     return row_ptr, cols, order, np.array(flags, np.int32)
 
 
-def _check(h, M, grid, tile, **mask):
+def _check(h, M, grid, tile, mode=0, **mask):
     L = sa.sparse_attn_layout(h)
     counts = oracle.tile_counts(grid, tile)
-    row_ptr, cols, order, flags = _expected(M, L, counts)
+    row_ptr, cols, order, flags = _expected(M, L, counts, mode)
     heads = M.shape[0]
     P = heads * L["pairs"]
     mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
@@ -124,14 +134,15 @@ PAIR_GRIDS = [
 
 @pytest.mark.parametrize("grid,tile", PAIR_GRIDS)
 @pytest.mark.parametrize("density", [0.0, 0.3, 1.0])
-def test_random_bitmap_pair_lists_bit_exact(grid, tile, density):
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+def test_random_bitmap_pair_lists_bit_exact(grid, tile, density, pairing):
     heads = 3
     nT = oracle.num_tiles(grid, tile)
     rng = np.random.default_rng([7, int(density * 10), *grid])
     M = (rng.random((heads, nT, nT)) < density).astype(np.uint8)
-    print(f"pair lists grid={grid} density={density}", flush=True)
-    h = sa.sparse_attn_create(heads, 128, grid, tile, "bf16")
-    _check(h, M, grid, tile, bitmap=M)
+    print(f"pair lists grid={grid} density={density} pairing={pairing}", flush=True)
+    h = sa.sparse_attn_create(heads, 128, grid, tile, "bf16", pairing=pairing)
+    _check(h, M, grid, tile, mode=sa._PAIRINGS[pairing], bitmap=M)
 
 
 def test_pair_lists_need_the_matrix_core_kernel():
