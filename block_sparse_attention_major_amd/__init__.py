@@ -175,7 +175,8 @@ class Handle:
         return self._sizes
 
     def __del__(self):
-        if getattr(self, "ptr", None):
+        # At interpreter exit the module's globals may already be gone.
+        if getattr(self, "ptr", None) and _lib is not None:
             _lib.sparse_attn_destroy(self.ptr)
             self.ptr = None
 
