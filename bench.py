@@ -416,7 +416,7 @@ def main():
     elem = 2
     attn_tflops = F / (attn_ms * 1e-3) / 1e12
     in_bytes = heads * N * d * elem
-    slot_bytes = heads * info["nT"] * info["tile_volume"] * d * elem
+    slot_bytes = heads * sa.sparse_attn_layout(h)["slots"] * d * elem
     perm_bytes = 2 * (in_bytes + slot_bytes)  # K and V: raster read, tile-major written
     traffic = traffic_per_launch(args.workload)
     result = {

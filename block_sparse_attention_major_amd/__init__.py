@@ -71,7 +71,8 @@ class sparse_attn_config(ctypes.Structure):
     _fields_ = [("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("grid", ctypes.c_int32 * 3), ("tile", ctypes.c_int32 * 3),
                 ("dtype", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
-                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32),
+                ("vector_alu", ctypes.c_int32)]
 
 
 class sparse_attn_window_group(ctypes.Structure):
@@ -93,7 +94,8 @@ class sparse_attn_layout_info(ctypes.Structure):
                 ("ws_offset_v", ctypes.c_size_t), ("ws_offset_o", ctypes.c_size_t),
                 ("ws_bytes", ctypes.c_size_t), ("pair_axis", ctypes.c_int32),
                 ("pair_grid", ctypes.c_int32 * 3), ("pairs", ctypes.c_int64),
-                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32)]
+                ("order", ctypes.c_int32), ("pairing", ctypes.c_int32),
+                ("slot_stride", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -246,10 +248,12 @@ def _nbytes(t):
 
 
 def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0,
-                       order=SPARSE_ATTN_ORDER_TILES, pairing=SPARSE_ATTN_PAIRING_AUTO):
+                       order=SPARSE_ATTN_ORDER_TILES, pairing=SPARSE_ATTN_PAIRING_AUTO,
+                       vector_alu=False):
     """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32; order:
     "tiles"/"hilbert" or SPARSE_ATTN_ORDER_*; pairing: "auto"/"overlap"/
-    "all"/"none" or SPARSE_ATTN_PAIRING_*."""
+    "all"/"none" or SPARSE_ATTN_PAIRING_*; vector_alu: run bf16 on the
+    vector-ALU kernel instead of the matrix-core kernels."""
     if isinstance(dtype, str):
         dtype = {"bf16": SPARSE_ATTN_BF16, "f32": SPARSE_ATTN_F32}[dtype]
     if isinstance(order, str):
@@ -258,7 +262,7 @@ def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0,
         pairing = _PAIRINGS[pairing]
     cfg = sparse_attn_config(int(heads), int(head_dim), (ctypes.c_int32 * 3)(*grid),
                              (ctypes.c_int32 * 3)(*tile), int(dtype), float(softmax_scale),
-                             int(order), int(pairing))
+                             int(order), int(pairing), int(bool(vector_alu)))
     out = _vp()
     st = _lib.sparse_attn_create(ctypes.byref(cfg), ctypes.byref(out))
     if st != SPARSE_ATTN_OK:

@@ -45,13 +45,13 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
     const int r = P.rows.order[blockIdx.x];
     const int h = r / L.nT, i = r - h * L.nT;
     const int ci = tile_real_count(L, i);
-    const bool active = slot < L.B && slot < ci;
+    const bool active = slot < L.S && slot < ci;
     const float sl2 = P.scale_log2;
 
     // Row of this slot's query in q and o: the raster token (raster I/O) or
     // the tile-major slot.
     const int tok = (active && (P.raster || P.lse)) ? raster_token(L, i, slot) : 0;
-    const long long qrow = P.raster ? (long long)h * L.N + tok : (long long)h * L.Npad + (long long)i * L.B + slot;
+    const long long qrow = P.raster ? (long long)h * L.N + tok : (long long)h * L.Npad + (long long)i * L.S + slot;
     float q[DH], o[DH];
 #pragma unroll
     for (int e = 0; e < DH; ++e) {
@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads) void attn_generic_kernel(Layout L, AttnPa
     for (int idx = beg; idx < end; ++idx) {
         const int j = P.rows.cols[idx];
         const int cj = tile_real_count(L, j);
-        const long long krow0 = (long long)h * L.Npad + (long long)j * L.B;
+        const long long krow0 = (long long)h * L.Npad + (long long)j * L.S;
         for (int k0 = 0; k0 < cj; k0 += kChunk) {
             const int kn = min(kChunk, cj - k0);
             __syncthreads();

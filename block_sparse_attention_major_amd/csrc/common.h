@@ -4,11 +4,13 @@
 // family; Fig. 3 caption: masks run in block-sparse attention kernels).  The
 // T x H x W token grid (raster token id n = (t H + y) W + x) is cut into
 // tt x th x tw tiles, numbered raster over the tile grid (nt, ny, nx).  Tiles
-// at the far edges are clipped.  Tile tau owns slots [tau B, tau B + B) of
-// the tile-major layout, B = tt th tw; its c_tau real tokens fill the first
-// c_tau slots in raster order over the clipped tile, and the remaining slots
-// are empty (zero in permuted inputs, never read back from outputs).  One
-// tile is one block of the attention kernel.
+// at the far edges are clipped.  Tile tau owns slots [tau S, tau S + S) of
+// the tile-major layout: S = 128 for the bf16 matrix-core kernels (whatever
+// the tile volume tt th tw <= 128), S = tt th tw for the vector-ALU kernel.
+// Its c_tau real tokens fill the first c_tau slots in raster order over the
+// clipped tile, and the remaining slots are empty (zero in permuted inputs,
+// never read back from outputs).  One tile is one block of the attention
+// kernel.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,11 +25,11 @@ struct Layout {
     int tt, th, tw;   // tile shape
     int nt, ny, nx;   // tile grid
     int nT;           // tiles
-    int B;            // slots per tile
+    int S;            // slots per tile
     int heads;
     int D;            // head dim
     long long N;      // tokens
-    long long Npad;   // slots = nT * B
+    long long Npad;   // slots = nT * S
     // Query-tile pairs.  The matrix-core kernel runs two query tiles of one
     // head per workgroup, over the union of their key lists.  Tiles pair up
     // along axis pax (0 = t, 1 = y, 2 = x) as coordinates (2c, 2c + 1); a

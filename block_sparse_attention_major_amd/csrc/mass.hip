@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
     bf16x8 qf[KS];
     if (wave_active) {
         const bf16x8 *qp =
-            (const bf16x8 *)(Qt + ((long long)h * L.Npad + (long long)i * L.B + slot) * D);
+            (const bf16x8 *)(Qt + ((long long)h * L.Npad + (long long)i * L.S + slot) * D);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qf[ks] = qp[2 * ks + hi];

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(Layout L, int vp
     const int tau = blockIdx.x - h * L.nT;
     const TileBox bx = tile_box(L, tau);
     const long long raster0 = (long long)h * L.N;
-    const long long slot0 = (long long)h * L.Npad + (long long)tau * L.B;
+    const long long slot0 = (long long)h * L.Npad + (long long)tau * L.S;
     if (L.seq_tok) {
         // Hilbert order: consecutive slots hold tokens scattered over the
         // raster, so each slot row is copied on its own (still 16-byte
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(Layout L, int vp
     if (DIR == 0) {
         const int c = bx.et * bx.ey * bx.ex;
         uint4 *pad = dst + (slot0 + c) * vpr;
-        const int nvec = (L.B - c) * vpr;
+        const int nvec = (L.S - c) * vpr;
         for (int v = threadIdx.x; v < nvec; v += kThreads)
             pad[v] = make_uint4(0, 0, 0, 0);
     }
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void permute_tile_columns_kernel(
     const int tau = blockIdx.x - h * L.nT;
     const TileBox bx = tile_box(L, tau);
     const int c = bx.et * bx.ey * bx.ex;
-    const int B = L.B;
+    const int B = L.S;  // slots per tile
     const uint4 *rows = reinterpret_cast<const uint4 *>(src + (long long)h * L.N * D);
     for (int u = threadIdx.x; u < B * CPR; u += kThreads) {
         const int slot = u / CPR, ch = u - slot * CPR;

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(Layout L, const T *_
     const int ht = blockIdx.x;
     const int h = ht / L.nT, tau = ht - h * L.nT;
     const int c = tile_real_count(L, tau);
-    const T *src = (blockIdx.y == 0 ? q : k) + ((long long)h * L.Npad + (long long)tau * L.B) * D;
+    const T *src = (blockIdx.y == 0 ? q : k) + ((long long)h * L.Npad + (long long)tau * L.S) * D;
     float *dst = (blockIdx.y == 0 ? qbar : kbar) + (long long)ht * D;
     const int g = threadIdx.x % G, r0 = threadIdx.x / G;
     float acc[8];

@@ -446,12 +446,17 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     if (nT * nT * c.heads >= (1ll << 31))
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED,
                     "heads * tiles^2 = %lld does not fit 32-bit index lists", nT * nT * c.heads);
+    // bf16 runs on the matrix-core kernels, whose blocks are 128 slots for
+    // any tile volume (a smaller tile leaves slots empty); fp32, or bf16 on
+    // request, runs on the vector-ALU kernel with B slots per tile.
+    const int kernel = (c.dtype == SPARSE_ATTN_BF16 && !c.vector_alu) ? SPARSE_ATTN_KERNEL_MFMA_BF16
+                                                                     : SPARSE_ATTN_KERNEL_GENERIC;
     L.nT = (int)nT;
-    L.B = (int)B;
+    L.S = kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? 128 : (int)B;
     L.heads = c.heads;
     L.D = c.head_dim;
     L.N = N;
-    L.Npad = nT * B;
+    L.Npad = nT * L.S;
     // Pair query tiles along y, t or x: an axis of even extent first (no
     // tile left alone), preferring y, then t, then x.
     {
@@ -475,8 +480,7 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     if (c.order == SPARSE_ATTN_ORDER_HILBERT)
         h->seq = hilbert_sequence(c.grid[0], c.grid[1], c.grid[2], cube_k);
     h->elem_bytes = c.dtype == SPARSE_ATTN_F32 ? 4 : 2;
-    h->kernel = (c.dtype == SPARSE_ATTN_BF16 && B == 128) ? SPARSE_ATTN_KERNEL_MFMA_BF16
-                                                          : SPARSE_ATTN_KERNEL_GENERIC;
+    h->kernel = kernel;
     h->scale = c.softmax_scale > 0.f ? c.softmax_scale : 1.0f / std::sqrt((float)c.head_dim);
     *out = h;
     return SPARSE_ATTN_OK;
@@ -494,7 +498,8 @@ int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *inf
     info->tile_grid[0] = h->L.nt;
     info->tile_grid[1] = h->L.ny;
     info->tile_grid[2] = h->L.nx;
-    info->tile_volume = h->L.B;
+    info->tile_volume = h->L.tt * h->L.th * h->L.tw;
+    info->slot_stride = h->L.S;
     info->slots = h->L.Npad;
     info->kernel = h->kernel;
     info->v_layout = h->kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? SPARSE_ATTN_LAYOUT_TILE_COLUMNS
@@ -865,7 +870,7 @@ int sparse_attn_tile_mass(sparse_attn_handle *h, const void *q, const void *k, v
     if (!mass || !aligned16(mass))
         return fail(h, SPARSE_ATTN_INVALID_ARG, "mass must be non-null and 16-byte aligned");
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
-        return fail(h, SPARSE_ATTN_UNSUPPORTED, "the tile mass runs on the matrix-core path (bf16, B = 128)");
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "the tile mass runs on the matrix-core path (bf16)");
     const sa::Layout &L = h->L;
     const size_t n = io_bytes(h), mb = size_t(L.heads) * L.nT * L.nT * sizeof(float);
     const WsLayout w = ws_layout(h);
@@ -933,7 +938,7 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
     const size_t means = sa::align256(size_t(L.heads) * L.nT * L.D * 4);
     if (2 * means + 4 * size_t(L.heads) > w.total - w.o)
         return fail(h, SPARSE_ATTN_UNSUPPORTED, "tiles of %d slots are too small for the selection scratch",
-                    L.B);
+                    L.S);
     char *b = static_cast<char *>(ws);
     float *qbar = reinterpret_cast<float *>(b + w.o);
     float *kbar = reinterpret_cast<float *>(b + w.o + means);
@@ -962,7 +967,7 @@ int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32
     if (layout == SPARSE_ATTN_LAYOUT_ROWS) {
         e = sa::launch_permute_rows(h->L, h->elem_bytes, src, dst, s);
     } else if (layout == SPARSE_ATTN_LAYOUT_TILE_COLUMNS) {
-        if (h->elem_bytes != 2 || h->L.B % 8 != 0)
+        if (h->elem_bytes != 2 || h->L.S % 8 != 0)
             return fail(h, SPARSE_ATTN_UNSUPPORTED,
                         "tile-column layout needs bf16 and a tile volume divisible by 8");
         e = sa::launch_permute_tile_columns(h->L, src, dst, s);

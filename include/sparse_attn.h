@@ -75,17 +75,23 @@ enum { SPARSE_ATTN_MASK_BITMAP = 0, SPARSE_ATTN_MASK_DUAL_WINDOW = 1 };
 
 /* Layouts of a permuted tensor (sparse_attn_permute). */
 enum {
-    /* [heads][nT * B][head_dim]: slot-major rows, one row per slot. */
+    /* [heads][nT * S][head_dim]: slot-major rows, one row per slot (S =
+     * sparse_attn_layout_info.slot_stride slots per tile). */
     SPARSE_ATTN_LAYOUT_ROWS = 0,
-    /* [heads][nT][head_dim][B]: per tile, one row of B slots per feature
+    /* [heads][nT][head_dim][S]: per tile, one row of S slots per feature
      * (the transposed value tile the MFMA kernel reads). */
     SPARSE_ATTN_LAYOUT_TILE_COLUMNS = 1
 };
 
 /* Attention kernels forward may select (sparse_attn_layout_info.kernel). */
 enum {
-    SPARSE_ATTN_KERNEL_MFMA_BF16 = 0, /* bf16 matrix-core kernel: B = 128, head_dim 64 or 128 */
-    SPARSE_ATTN_KERNEL_GENERIC = 1    /* fp32 vector-ALU kernel: any supported shape */
+    /* bf16 matrix-core kernels: any tile volume B <= 128, head_dim 64 or
+     * 128; every tile takes S = 128 slots (a tile of B < 128 tokens leaves
+     * 128 - B of them empty, and that share of the matrix work idle). */
+    SPARSE_ATTN_KERNEL_MFMA_BF16 = 0,
+    /* vector-ALU kernel: fp32 always, bf16 on request
+     * (sparse_attn_config.vector_alu); S = B slots per tile. */
+    SPARSE_ATTN_KERNEL_GENERIC = 1
 };
 
 /*
@@ -147,6 +153,9 @@ typedef struct sparse_attn_config {
     float softmax_scale;   /* score scale s; 0 selects 1 / sqrt(head_dim) */
     int32_t order;         /* SPARSE_ATTN_ORDER_TILES (0) or SPARSE_ATTN_ORDER_HILBERT */
     int32_t pairing;       /* SPARSE_ATTN_PAIRING_* (0 = AUTO) */
+    /* Nonzero runs bf16 on the vector-ALU kernel instead of the matrix-core
+     * kernels (for comparison and testing); fp32 always runs there. */
+    int32_t vector_alu;
 } sparse_attn_config;
 
 /*
@@ -184,8 +193,8 @@ typedef struct sparse_attn_layout_info {
     int64_t tokens;        /* N = T * H * W */
     int64_t tiles;         /* nT = nt * ny * nx */
     int32_t tile_grid[3];  /* nt, ny, nx = ceil(T / tt), ceil(H / th), ceil(W / tw) */
-    int32_t tile_volume;   /* B = tt * th * tw: slots per tile */
-    int64_t slots;         /* N_pad = nT * B */
+    int32_t tile_volume;   /* B = tt * th * tw: tokens in a whole tile */
+    int64_t slots;         /* N_pad = nT * S: rows of a tile-major tensor */
     int32_t kernel;        /* SPARSE_ATTN_KERNEL_* that forward runs */
     int32_t v_layout;      /* SPARSE_ATTN_LAYOUT_* of the permuted V in the workspace */
     /* Byte offsets of the permuted Q, K, V and of the tile-major output O
@@ -202,6 +211,10 @@ typedef struct sparse_attn_layout_info {
     /* The pairing in effect (OVERLAP, ALL or NONE; AUTO resolved), or -1
      * for the vector-ALU kernel. */
     int32_t pairing;
+    /* S: slots per tile in the tile-major layout, 128 for the matrix-core
+     * kernels, B for the vector-ALU kernel.  Tile tau owns slots
+     * [tau S, tau S + S); empty ones are zero in permuted inputs. */
+    int32_t slot_stride;
 } sparse_attn_layout_info;
 
 typedef struct sparse_attn_handle sparse_attn_handle;
@@ -210,7 +223,8 @@ typedef struct sparse_attn_handle sparse_attn_handle;
  * Validate a configuration and plan the tile layout (host only, no device
  * call).  Tiles are numbered raster over the tile grid (t, then y, then x);
  * tiles at the far edges of a grid the tile does not divide are clipped.
- * Each tile owns B consecutive slots: its c real tokens fill the first c in
+ * Each tile owns S consecutive slots (S = 128 on the matrix-core kernels,
+ * B = tt th tw on the vector-ALU kernel): its c real tokens fill the first c in
  * raster order over the clipped tile, the rest are empty.
  * Errors: INVALID_ARG (null, non-positive sizes, bad dtype, order or pairing),
  * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31,
@@ -310,7 +324,7 @@ int sparse_attn_forward_lse(sparse_attn_handle *h, const void *q, const void *k,
  * call on each device (the device current at the call); the stream must
  * belong to that device.  Same arguments, results and errors as
  * sparse_attn_forward, plus UNSUPPORTED when the permuted K and V need more
- * than the array holds (2 * heads * tiles * B * head_dim * element bytes,
+ * than the array holds (2 * heads * slots * head_dim * element bytes,
  * each half rounded up to 256 bytes); the scratch check comes before the
  * mask check.  Every call on a device shares that device's array: calls
  * that overlap in time on one device (other streams, other threads) race
@@ -351,7 +365,7 @@ int sparse_attn_unpermute_output(sparse_attn_handle *h, void *ws, size_t ws_byte
  * first) and uses the output region of ws as scratch.  k_per_head: host
  * int32 [heads], each in 0..nT.  bitmap: device uint8 [heads][nT][nT], out.
  * Errors: INVALID_ARG (null pointers, k out of range), UNSUPPORTED (more
- * than 8192 tiles, or tiles too small for the scratch: B * elem < 8 bytes),
+ * than 8192 tiles, or tiles too small for the scratch: S * elem < 8 bytes),
  * WORKSPACE_TOO_SMALL, HIP_ERROR.
  */
 int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, void *ws,
@@ -369,8 +383,8 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
  * forward workspace (its Q and K regions are overwritten); mass: device fp32
  * [heads][nT][nT], out.  This is dense work (two passes of Q K^T over every
  * key); it is meant for offline calibration, not the forward path.
- * Errors: INVALID_ARG, UNSUPPORTED (needs the matrix-core path: bf16,
- * B = 128), WORKSPACE_TOO_SMALL, NO_ORDER, HIP_ERROR.
+ * Errors: INVALID_ARG, UNSUPPORTED (needs the matrix-core path: bf16 and
+ * not vector_alu), WORKSPACE_TOO_SMALL, NO_ORDER, HIP_ERROR.
  */
 int sparse_attn_tile_mass(sparse_attn_handle *h, const void *q, const void *k, void *ws,
                           size_t ws_bytes, float *mass, void *stream);
@@ -413,9 +427,9 @@ int sparse_attn_search_windows(sparse_attn_handle *h, const float *mass,
 /*
  * Test hooks.
  * sparse_attn_permute: src [heads][N][head_dim] raster -> dst in `layout`
- *   (SPARSE_ATTN_LAYOUT_*), empty slots zero.  dst holds heads * nT * B *
- *   head_dim elements.
- * sparse_attn_unpermute: src [heads][nT * B][head_dim] rows -> dst
+ *   (SPARSE_ATTN_LAYOUT_*), empty slots zero.  dst holds heads * nT * S *
+ *   head_dim elements (S = the layout's slot_stride).
+ * sparse_attn_unpermute: src [heads][nT * S][head_dim] rows -> dst
  *   [heads][N][head_dim] raster; empty slots are not read.
  * sparse_attn_read_index_lists: copy the compiled row offsets (int32
  *   [heads nT + 1]), index list (int32, first min(nnz, cols_capacity)

@@ -50,7 +50,7 @@ def test_create_and_layout(sa):
     h = sa.sparse_attn_create(40, 128, (21, 45, 80), (1, 8, 16), "bf16")
     L = sa.sparse_attn_layout(h)
     assert L["tokens"] == 75600 and L["tiles"] == 630 and L["tile_grid"] == [21, 6, 5]
-    assert L["tile_volume"] == 128 and L["slots"] == 80640
+    assert L["tile_volume"] == 128 and L["slot_stride"] == 128 and L["slots"] == 80640
     assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16
     assert L["v_layout"] == sa.SPARSE_ATTN_LAYOUT_TILE_COLUMNS
     per = 40 * 80640 * 128 * 2
@@ -64,9 +64,30 @@ def test_create_and_layout(sa):
     assert abs(shrink - 8 * (40 * 630 * 630 - 1000)) < 256
     sa.sparse_attn_destroy(h)
     tiny = sa.sparse_attn_create(2, 64, (4, 8, 8), (1, 4, 4), "f32")
-    assert sa.sparse_attn_layout(tiny)["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    L = sa.sparse_attn_layout(tiny)
+    assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC and L["pairing"] == -1
+    assert L["tile_volume"] == L["slot_stride"] == 16 and L["slots"] == 16 * 16
     full = sa.sparse_attn_mask_bytes(tiny)
     assert sa.sparse_attn_mask_bytes(tiny, 100) == full - 4 * (2 * 16 * 16 - 100)
+
+
+def test_small_bf16_tiles_take_matrix_core_blocks(sa):
+    # bf16 tiles of any volume run on the matrix cores in blocks of 128
+    # slots; vector_alu keeps them on the vector ALUs with B slots per tile.
+    h = sa.sparse_attn_create(3, 64, (3, 10, 12), (1, 4, 8), "bf16")
+    L = sa.sparse_attn_layout(h)
+    assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16
+    assert L["v_layout"] == sa.SPARSE_ATTN_LAYOUT_TILE_COLUMNS
+    assert L["tiles"] == 3 * 3 * 2 and L["tile_volume"] == 32 and L["slot_stride"] == 128
+    assert L["slots"] == 18 * 128 and L["ws_bytes"] == 4 * 3 * 18 * 128 * 64 * 2
+    v = sa.sparse_attn_create(3, 64, (3, 10, 12), (1, 4, 8), "bf16", vector_alu=True)
+    L = sa.sparse_attn_layout(v)
+    assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC and L["v_layout"] == sa.SPARSE_ATTN_LAYOUT_ROWS
+    assert L["tile_volume"] == L["slot_stride"] == 32 and L["slots"] == 18 * 32
+    # the Hilbert order: 1 x 1 x B tiles, still 128 slots each
+    hb = sa.sparse_attn_create(2, 128, (2, 16, 32), (1, 4, 16), "bf16", order="hilbert")
+    L = sa.sparse_attn_layout(hb)
+    assert L["tile_volume"] == 64 and L["slot_stride"] == 128 and L["slots"] == 16 * 128
 
 
 @pytest.mark.parametrize("grid,axis,pgrid", [

@@ -23,10 +23,10 @@ class Case:
     """Inputs of one forward: grid, tile, q/k/v (numpy), mask."""
 
     def __init__(self, grid, tile, q, k, v, dtype, bitmap=None, groups=None, gph=None, scale=0.0,
-                 pairing="auto"):
+                 pairing="auto", vector_alu=False):
         self.grid, self.tile, self.q, self.k, self.v = grid, tile, q, k, v
         self.dtype, self.bitmap, self.groups, self.gph, self.scale = dtype, bitmap, groups, gph, scale
-        self.pairing = pairing
+        self.pairing, self.vector_alu = pairing, vector_alu
         self.heads, self.N, self.d = q.shape
 
     @staticmethod
@@ -47,7 +47,8 @@ class Case:
 
 
 def gpu_forward(c, stages=False):
-    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing)
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing,
+                              vector_alu=c.vector_alu)
     mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
     if c.bitmap is not None:
         sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.bitmap))
@@ -120,7 +121,10 @@ def _random_case(grid, tile, d, dtype, heads=3, p=0.4, seed=0, empty_row=True, s
     ((3, 20, 36), (1, 8, 16), 64, "bf16"),    # head_dim 64 on the matrix cores
     ((1, 5, 7), (1, 8, 16), 128, "bf16"),     # one tile, larger than the grid
     ((2, 17, 33), (2, 4, 16), 128, "bf16"),   # clipped along t, y and x
-    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # B = 32: vector-ALU kernel
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # 32-token tiles in 128-slot blocks
+    ((3, 20, 36), (1, 8, 8), 128, "bf16"),    # 64-token tiles, clipped to 32
+    ((5, 10, 12), (2, 4, 8), 128, "bf16"),    # 64-token tiles clipped along t, y and x
+    ((2, 9, 11), (1, 3, 5), 64, "bf16"),      # 15-token tiles: one partial key block
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
     ((2, 5, 7), (2, 2, 3), 64, "f32"),
 ])
@@ -128,14 +132,33 @@ def _random_case(grid, tile, d, dtype, heads=3, p=0.4, seed=0, empty_row=True, s
 def test_ragged_shapes_with_empty_rows(grid, tile, d, dtype, pairing):
     c = _random_case(grid, tile, d, dtype)
     c.pairing = pairing
-    got, want, _ = full_check(c, f"ragged pairing={pairing}")
+    got, want, layout = full_check(c, f"ragged pairing={pairing}")
+    # bf16 runs on the matrix cores for every tile volume, in 128-slot blocks.
+    B = int(np.prod(tile))
+    assert layout["tile_volume"] == B
+    if dtype == "bf16":
+        assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16 and layout["slot_stride"] == 128
+    else:
+        assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC and layout["slot_stride"] == B
     nT = oracle.num_tiles(grid, tile)
     # the empty row (head 0, query tile nT // 2) outputs exactly zero
     perm, _ = oracle.perm(grid, tile)
-    B = int(np.prod(tile))
     toks = perm[(nT // 2) * B:(nT // 2 + 1) * B]
     toks = toks[toks >= 0]
     assert np.all(as_f64(got[0, toks]) == 0.0)
+
+
+@pytest.mark.parametrize("grid,tile,d", [
+    ((3, 20, 36), (1, 8, 16), 128),
+    ((3, 10, 12), (1, 4, 8), 64),
+])
+def test_bf16_on_the_vector_alu_kernel(grid, tile, d):
+    """bf16 inputs on the vector-ALU kernel (on request), tiles of B slots."""
+    c = _random_case(grid, tile, d, "bf16")
+    c.vector_alu = True
+    _, _, layout = full_check(c, "bf16 vector-ALU")
+    assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    assert layout["slot_stride"] == int(np.prod(tile))
 
 
 def test_explicit_scale():

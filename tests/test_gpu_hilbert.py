@@ -43,6 +43,7 @@ def _seq_view(grid, tile):
 @pytest.mark.parametrize("grid,tile,d,dtype", [
     ((3, 20, 36), (1, 8, 16), 128, "bf16"),
     ((2, 17, 33), (2, 4, 16), 64, "bf16"),
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # 32-token tiles in 128-slot blocks
     ((3, 10, 12), (1, 4, 8), 64, "f32"),
 ])
 def test_permutation_bit_exact(grid, tile, d, dtype):
@@ -50,24 +51,27 @@ def test_permutation_bit_exact(grid, tile, d, dtype):
     N = int(np.prod(grid))
     h = _handle(heads, d, grid, tile, dtype)
     L = sa.sparse_attn_layout(h)
-    B, nT = L["tile_volume"], L["tiles"]
+    B, S, nT = L["tile_volume"], L["slot_stride"], L["tiles"]
+    assert B == int(np.prod(tile)) and S == (128 if dtype == "bf16" else B)
     seq = oracle.hilbert_order(grid)
     x = _rand((heads, N, d), 5, dtype)
-    want = np.zeros((heads, nT * B, d), x.dtype)
-    want[:, :N] = x[:, seq]
+    # Rank r sits in slot r mod B of tile r // B, row (r // B) S + r mod B.
+    r = np.arange(N)
+    want = np.zeros((heads, nT * S, d), x.dtype)
+    want[:, (r // B) * S + r % B] = x[:, seq]
     xd = dev(x)
-    rows = torch.full((heads, nT * B, d), 7, dtype=xd.dtype, device="cuda")
+    rows = torch.full((heads, nT * S, d), 7, dtype=xd.dtype, device="cuda")
     sa.sparse_attn_permute(h, xd, rows, sa.SPARSE_ATTN_LAYOUT_ROWS)
     back = torch.zeros_like(xd)
     sa.sparse_attn_unpermute(h, rows, back)
     torch.cuda.synchronize()
     assert np.array_equal(host(rows, x), want)
     assert np.array_equal(host(back, x), x)
-    if dtype == "bf16" and B == 128:
-        cols = torch.full((heads, nT, d, B), 7, dtype=xd.dtype, device="cuda")
+    if dtype == "bf16":
+        cols = torch.full((heads, nT, d, S), 7, dtype=xd.dtype, device="cuda")
         sa.sparse_attn_permute(h, xd, cols, sa.SPARSE_ATTN_LAYOUT_TILE_COLUMNS)
         torch.cuda.synchronize()
-        wc = want.reshape(heads, nT, B, d).transpose(0, 1, 3, 2)
+        wc = want.reshape(heads, nT, S, d).transpose(0, 1, 3, 2)
         assert np.array_equal(host(cols, x), wc)
 
 
@@ -107,7 +111,7 @@ def _forward(h, q, k, v, M, lse=True, stages=False):
     ((3, 20, 36), (1, 8, 16), 128, "bf16"),   # pair + row kernels
     ((3, 20, 36), (1, 8, 16), 64, "bf16"),
     ((2, 17, 33), (2, 4, 16), 128, "bf16"),
-    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # B = 32: vector-ALU kernel
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # 32-token tiles in 128-slot blocks
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
 ])
 @pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])

@@ -26,9 +26,10 @@ def _rand(shape, seed, dtype):
 
 
 class Inputs:
-    def __init__(self, grid, tile, q, k, v, dtype, M, scale=0.0, pairing="auto"):
+    def __init__(self, grid, tile, q, k, v, dtype, M, scale=0.0, pairing="auto", vector_alu=False):
         self.grid, self.tile, self.q, self.k, self.v = grid, tile, q, k, v
         self.dtype, self.M, self.scale, self.pairing = dtype, M, scale, pairing
+        self.vector_alu = vector_alu
         self.heads, self.N, self.d = q.shape
 
     def oracle_scale(self):
@@ -36,17 +37,21 @@ class Inputs:
 
 
 def _random_inputs(grid, tile, d, dtype, heads=3, p=0.4, seed=0):
+    """dtype "bf16-vector": bf16 on the vector-ALU kernel."""
+    vector = dtype == "bf16-vector"
+    dtype = "bf16" if vector else dtype
     N = int(np.prod(grid))
     nT = oracle.num_tiles(grid, tile)
     q, k, v = (_rand((heads, N, d), seed + s, dtype) for s in (1, 2, 3))
     M = (np.random.default_rng(seed + 4).random((heads, nT, nT)) < p).astype(np.uint8)
     M[0, nT // 2, :] = 0  # a query tile that keeps nothing
-    return Inputs(grid, tile, q, k, v, dtype, M)
+    return Inputs(grid, tile, q, k, v, dtype, M, vector_alu=vector)
 
 
 def _gpu(c, mode):
     """o (numpy, input dtype) and lse (numpy fp32 or None) of one path."""
-    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing)
+    h = sa.sparse_attn_create(c.heads, c.d, c.grid, c.tile, c.dtype, c.scale, pairing=c.pairing,
+                              vector_alu=c.vector_alu)
     mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
     sa.sparse_attn_set_mask(h, mb, bitmap=dev(c.M))
     q, k, v = dev(c.q), dev(c.k), dev(c.v)
@@ -99,7 +104,9 @@ SHAPES = [
     ((3, 20, 36), (1, 8, 16), 64, "bf16"),    # head_dim 64 on the matrix cores
     ((1, 5, 7), (1, 8, 16), 128, "bf16"),     # one tile, larger than the grid
     ((2, 17, 33), (2, 4, 16), 128, "bf16"),   # clipped along t, y and x
-    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # B = 32: vector-ALU kernel
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # 32-token tiles in 128-slot blocks
+    ((5, 10, 12), (2, 4, 8), 128, "bf16"),    # 64-token tiles clipped along t, y and x
+    ((3, 10, 12), (1, 4, 8), 64, "bf16-vector"),  # bf16 on the vector-ALU kernel
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
     ((2, 5, 7), (2, 2, 3), 64, "f32"),
 ]
@@ -129,7 +136,7 @@ def test_lse_matches_the_oracle(grid, tile, d, dtype, pairing):
     o, lse = _gpu(c, "forward_lse")
     _check_lse(c, lse, "ragged")
     want = oracle.attention(c.grid, c.tile, c.q, c.k, c.v, c.M, scale=c.oracle_scale())
-    assert_close(as_f64(o), want, dtype, "ragged o")
+    assert_close(as_f64(o), want, c.dtype, "ragged o")
 
 
 @pytest.mark.parametrize("name", ["tiny", "small"])

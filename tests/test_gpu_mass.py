@@ -45,7 +45,8 @@ def _gpu_mass(q, k, grid, tile):
 
 
 @pytest.mark.parametrize("grid,tile,d", [((3, 20, 36), (1, 8, 16), 128), ((2, 17, 33), (2, 4, 16), 64),
-                                         ((4, 16, 16), (1, 8, 16), 128)])
+                                         ((4, 16, 16), (1, 8, 16), 128),
+                                         ((3, 10, 12), (1, 4, 8), 64)])  # 32-token tiles
 def test_mass_matches_the_oracle(grid, tile, d):
     heads = 2
     N = int(np.prod(grid))

@@ -18,6 +18,7 @@ GRIDS = [
     ((8, 30, 40), (1, 8, 16), 128, "bf16"),
     ((3, 20, 36), (1, 8, 16), 128, "bf16"),
     ((3, 20, 36), (1, 8, 16), 64, "bf16"),
+    ((3, 20, 36), (1, 4, 8), 128, "bf16"),    # 32-token tiles in 128-slot blocks
     ((1, 5, 7), (1, 8, 16), 128, "bf16"),
     ((3, 10, 12), (1, 4, 8), 64, "f32"),
     ((5, 3, 3), (2, 3, 3), 128, "f32"),
@@ -40,16 +41,24 @@ def test_permute_and_unpermute_bit_exact(grid, tile, d, dtype):
     nT = oracle.num_tiles(grid, tile)
     print(f"permute grid={grid} tile={tile} d={d} {dtype}", flush=True)
     x = _random_bits((heads, N, d), dtype, 1)
-    perm, pos = oracle.perm(grid, tile)
-    want = np.zeros((heads, nT * B, d), dtype=x.dtype)
-    real = perm >= 0
-    want[:, real] = x[:, perm[real]]
-
     h = sa.sparse_attn_create(heads, d, grid, tile, dtype)
     L = sa.sparse_attn_layout(h)
-    assert L["tiles"] == nT and L["slots"] == nT * B and L["tokens"] == N
+    # bf16 tiles take 128 slots whatever their volume (matrix-core blocks),
+    # fp32 tiles B.
+    S = 128 if dtype == "bf16" else B
+    assert L["tiles"] == nT and L["tile_volume"] == B and L["slot_stride"] == S
+    assert L["slots"] == nT * S and L["tokens"] == N
+    # The oracle's slot map has B slots per tile; slot s of tile t moves to
+    # t S + s.
+    perm, pos = oracle.perm(grid, tile)
+    want = np.zeros((heads, nT, S, d), dtype=x.dtype)
+    pm = perm.reshape(nT, B)
+    real = pm >= 0
+    want[:, :, :B][:, real] = x[:, pm[real]]
+    want = want.reshape(heads, nT * S, d)
+
     xd = dev(x)
-    rows = torch.full((heads, nT * B, d), 7, dtype=xd.dtype, device="cuda")  # pads must be zeroed
+    rows = torch.full((heads, nT * S, d), 7, dtype=xd.dtype, device="cuda")  # pads must be zeroed
     sa.sparse_attn_permute(h, xd, rows, sa.SPARSE_ATTN_LAYOUT_ROWS)
     got = host(rows, x)
     assert np.array_equal(got, want)
@@ -58,10 +67,10 @@ def test_permute_and_unpermute_bit_exact(grid, tile, d, dtype):
     sa.sparse_attn_unpermute(h, rows, back)
     assert np.array_equal(host(back, x), x)
 
-    if dtype == "bf16" and B % 8 == 0:
-        cols = torch.full((heads, nT, d, B), 5, dtype=xd.dtype, device="cuda")
+    if dtype == "bf16":
+        cols = torch.full((heads, nT, d, S), 5, dtype=xd.dtype, device="cuda")
         sa.sparse_attn_permute(h, xd, cols, sa.SPARSE_ATTN_LAYOUT_TILE_COLUMNS)
-        want_cols = want.reshape(heads, nT, B, d).transpose(0, 1, 3, 2)
+        want_cols = want.reshape(heads, nT, S, d).transpose(0, 1, 3, 2)
         assert np.array_equal(host(cols, x), want_cols)
 
 

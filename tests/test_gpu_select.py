@@ -109,6 +109,7 @@ def test_hunyuan_masks_match_the_oracle():
 @pytest.mark.parametrize("grid,tile,d,dtype", [
     ((4, 8, 8), (1, 4, 4), 64, "f32"),
     ((3, 20, 36), (1, 8, 16), 128, "bf16"),
+    ((3, 10, 12), (1, 4, 8), 64, "bf16"),      # 32-token tiles in 128-slot blocks
     ((5, 3, 3), (2, 3, 3), 64, "f32"),
 ])
 def test_random_inputs_match_the_oracle(grid, tile, d, dtype):
