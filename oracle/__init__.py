@@ -51,9 +51,9 @@ def _load():
         lib.oracle_select_topk.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_double, ctypes.c_void_p, ctypes.c_int]
-        lib.oracle_hilbert_index.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                             ctypes.c_int64]
-        lib.oracle_hilbert_index.restype = ctypes.c_uint64
+        lib.oracle_hilbert_point.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.POINTER(ctypes.c_int64),
+                                             ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+        lib.oracle_hilbert_point.restype = None
         lib.oracle_hilbert_order.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                              ctypes.c_void_p]
         lib.oracle_tile_mass.argtypes = [g, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
@@ -102,9 +102,11 @@ def perm(grid, tile):
     return p, q
 
 
-def hilbert_index(k, t, y, x):
-    """Index of cell (t, y, x) on the 3D Hilbert curve over a 2^k cube."""
-    return int(_load().oracle_hilbert_index(int(k), int(t), int(y), int(x)))
+def hilbert_point(k, h):
+    """Cell (t, y, x) at index h of the 3D Hilbert curve over a 2^k cube."""
+    t, y, x = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _load().oracle_hilbert_point(int(k), int(h), ctypes.byref(t), ctypes.byref(y), ctypes.byref(x))
+    return t.value, y.value, x.value
 
 
 def hilbert_order(grid):

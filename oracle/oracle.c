@@ -128,14 +128,23 @@ void oracle_perm(const oracle_grid *g, int64_t *perm, int64_t *pos)
  * Hilbert-curve token order (DFSAttn page, abstract: tokens are reordered
  * along a Hilbert curve so that runs of consecutive tokens are compact in
  * space, which keeps block-sparse execution efficient at a finer grain).
- * The page gives no construction; the one used here is the 3D Hilbert curve
- * of J. Skilling, "Programming the Hilbert curve", AIP Conf. Proc. 707
- * (2004), over the smallest cube of side 2^k that holds the grid, with axes
- * (t, y, x): the coordinates are turned into Skilling's transposed index,
- * whose bits are then read level by level from the top, t's bit first.
- * Tokens are ranked by that index (cube points outside the grid are
- * skipped); runs of B consecutive ranks then take the place of tiles, so
- * the layout is the tile layout of a 1 x 1 x N grid in rank order.
+ * The page gives no construction; the curve used is the 3D Hilbert curve of
+ * J. Skilling, "Programming the Hilbert curve", AIP Conf. Proc. 707 (2004),
+ * over the smallest cube of side 2^k that holds the grid, axes (t, y, x),
+ * its 3k index bits read level by level from the top with t's bit first.
+ *
+ * The oracle walks the curve from index to point.  Skilling's point-to-index
+ * map ends by reading the interleaved coordinate bits (after its per-level
+ * exchanges) as a Gray code and decoding it, so from an index h the
+ * interleaved bits are the Gray code h ^ (h >> 1), dealt back to the axes.
+ * The per-level steps are then undone in reverse: each exchange or
+ * reflection of the bits below level Q is its own inverse, and the bit it
+ * tests (bit Q of an axis) is not changed by the steps of level Q and
+ * below, so the steps are replayed from the lowest level up, within a level
+ * from the last axis to the first.  The order of a grid lists the cube's
+ * points in index order, skipping those outside the grid; runs of B
+ * consecutive ranks then take the place of tiles, so the layout is the tile
+ * layout of a 1 x 1 x N grid in rank order.
  */
 static int cube_order(int64_t T, int64_t H, int64_t W)
 {
@@ -148,66 +157,44 @@ static int cube_order(int64_t T, int64_t H, int64_t W)
     return k;
 }
 
-uint64_t oracle_hilbert_index(int k, int64_t t, int64_t y, int64_t x)
+/* The point (t, y, x) of index h on the curve over the 2^k cube. */
+void oracle_hilbert_point(int k, uint64_t h, int64_t *t, int64_t *y, int64_t *x)
 {
-    if (k == 0)
-        return 0;
-    uint64_t X[3] = {(uint64_t)t, (uint64_t)y, (uint64_t)x};
-    /* Walk the levels from the top; at each, a set bit of axis i reflects
-     * the lower bits of axis 0, a clear bit swaps them between axes 0 and i. */
-    for (uint64_t Q = (uint64_t)1 << (k - 1); Q > 1; Q >>= 1) {
-        uint64_t low = Q - 1;
-        for (int i = 0; i < 3; ++i) {
+    const uint64_t gray = h ^ (h >> 1);
+    uint64_t X[3] = {0, 0, 0};
+    /* Bit 3 b + 2 - i of the index belongs to axis i at level b. */
+    for (int b = 0; b < k; ++b)
+        for (int i = 0; i < 3; ++i)
+            X[i] |= ((gray >> (3 * b + 2 - i)) & 1) << b;
+    for (int b = 1; b < k; ++b) {
+        const uint64_t Q = (uint64_t)1 << b, low = Q - 1;
+        for (int i = 2; i >= 0; --i) {
             if (X[i] & Q) {
-                X[0] ^= low;
+                X[0] ^= low; /* reflection of axis 0's lower bits */
             } else {
-                uint64_t d = (X[0] ^ X[i]) & low;
+                uint64_t d = (X[0] ^ X[i]) & low; /* exchange with axis i */
                 X[0] ^= d;
                 X[i] ^= d;
             }
         }
     }
-    /* Gray-code step across the axes, then the correction of the lower bits. */
-    X[1] ^= X[0];
-    X[2] ^= X[1];
-    uint64_t flip = 0;
-    for (uint64_t Q = (uint64_t)1 << (k - 1); Q > 1; Q >>= 1)
-        if (X[2] & Q)
-            flip ^= Q - 1;
-    for (int i = 0; i < 3; ++i)
-        X[i] ^= flip;
-    uint64_t h = 0;
-    for (int b = k - 1; b >= 0; --b)
-        for (int i = 0; i < 3; ++i)
-            h = (h << 1) | ((X[i] >> b) & 1);
-    return h;
-}
-
-typedef struct {
-    uint64_t key;
-    int64_t token;
-} keyed_token;
-
-static int cmp_keyed(const void *pa, const void *pb)
-{
-    const keyed_token *a = (const keyed_token *)pa, *b = (const keyed_token *)pb;
-    return a->key < b->key ? -1 : a->key > b->key ? 1 : 0;
+    *t = (int64_t)X[0];
+    *y = (int64_t)X[1];
+    *x = (int64_t)X[2];
 }
 
 /* seq[r] = raster token of Hilbert rank r, for r in [0, T H W). */
 void oracle_hilbert_order(int64_t T, int64_t H, int64_t W, int64_t *seq)
 {
-    int64_t N = T * H * W;
-    int k = cube_order(T, H, W);
-    keyed_token *kt = (keyed_token *)malloc(sizeof(keyed_token) * (size_t)N);
-    for (int64_t n = 0; n < N; ++n) {
-        kt[n].key = oracle_hilbert_index(k, n / (H * W), (n / W) % H, n % W);
-        kt[n].token = n;
+    const int k = cube_order(T, H, W);
+    const uint64_t cells = (uint64_t)1 << (3 * k);
+    int64_t r = 0;
+    for (uint64_t h = 0; h < cells; ++h) {
+        int64_t t, y, x;
+        oracle_hilbert_point(k, h, &t, &y, &x);
+        if (t < T && y < H && x < W)
+            seq[r++] = (t * H + y) * W + x;
     }
-    qsort(kt, (size_t)N, sizeof(keyed_token), cmp_keyed);
-    for (int64_t r = 0; r < N; ++r)
-        seq[r] = kt[r].token;
-    free(kt);
 }
 
 /*

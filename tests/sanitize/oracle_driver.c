@@ -23,7 +23,7 @@ typedef struct {
 int64_t oracle_num_tiles(const oracle_grid *g);
 void oracle_tile_counts(const oracle_grid *g, int64_t *counts);
 void oracle_perm(const oracle_grid *g, int64_t *perm, int64_t *pos);
-uint64_t oracle_hilbert_index(int k, int64_t t, int64_t y, int64_t x);
+void oracle_hilbert_point(int k, uint64_t h, int64_t *t, int64_t *y, int64_t *x);
 void oracle_hilbert_order(int64_t T, int64_t H, int64_t W, int64_t *seq);
 void oracle_mask_from_windows(const oracle_grid *g, int64_t heads, const oracle_group *groups,
                               const int32_t *groups_per_head, uint8_t *M);
@@ -190,10 +190,11 @@ int main(void)
         free(seq);
         free(seen);
     }
-    for (int64_t t = 0; t < 8; ++t)
-        for (int64_t y = 0; y < 8; ++y)
-            for (int64_t x = 0; x < 8; ++x)
-                EXPECT(oracle_hilbert_index(3, t, y, x) < 512);
+    for (uint64_t hh = 0; hh < 512; ++hh) {
+        int64_t t, y, x;
+        oracle_hilbert_point(3, hh, &t, &y, &x);
+        EXPECT(t >= 0 && t < 8 && y >= 0 && y < 8 && x >= 0 && x < 8);
+    }
     printf("oracle checks done, %d failure(s)\n", fails);
     return fails ? 1 : 0;
 }

@@ -15,15 +15,11 @@ import oracle
 
 
 def _cells(k):
+    """idx[t, y, x] (index of each cell) and pos[h] (cell of each index)."""
     n = 1 << k
-    idx = np.empty((n, n, n), dtype=np.int64)
-    for t in range(n):
-        for y in range(n):
-            for x in range(n):
-                idx[t, y, x] = oracle.hilbert_index(k, t, y, x)
-    pos = np.empty((n ** 3, 3), dtype=np.int64)
-    pos[idx.reshape(-1)] = np.stack(np.meshgrid(np.arange(n), np.arange(n), np.arange(n),
-                                                indexing="ij"), axis=-1).reshape(-1, 3)
+    pos = np.array([oracle.hilbert_point(k, h) for h in range(n ** 3)], dtype=np.int64)
+    idx = np.full((n, n, n), -1, dtype=np.int64)
+    idx[pos[:, 0], pos[:, 1], pos[:, 2]] = np.arange(n ** 3)
     return idx, pos
 
 
@@ -38,6 +34,7 @@ def test_order_one_is_the_reflected_gray_code():
 def test_bijective_continuous_and_nested(k):
     idx, pos = _cells(k)
     n = 1 << k
+    assert pos.min() >= 0 and pos.max() < n
     assert np.array_equal(np.sort(idx.reshape(-1)), np.arange(n ** 3))
     assert tuple(pos[0]) == (0, 0, 0)
     steps = np.abs(np.diff(pos, axis=0)).sum(axis=1)
@@ -58,7 +55,8 @@ def test_grid_order_ranks_cells_by_cube_index(grid):
     k = int(np.ceil(np.log2(max(grid)))) if max(grid) > 1 else 0
     seq = oracle.hilbert_order(grid)
     assert np.array_equal(np.sort(seq), np.arange(N))
-    keys = [oracle.hilbert_index(k, n // (H * W), (n // W) % H, n % W) for n in range(N)]
+    idx, _ = _cells(k)
+    keys = [idx[n // (H * W), (n // W) % H, n % W] for n in range(N)]
     assert np.array_equal(seq, np.argsort(keys, kind="stable"))
 
 
