@@ -244,6 +244,61 @@ def gemm_reference(stream, n=16384, reps=5):
     return {"shape": [n, n, n], "ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
 
 
+def tile_volume_sweep(sa, seed=1, reps=5):
+    """Attention stage of layouts of several tile volumes on the Wan grid
+    (4 heads), bf16 on the matrix-core kernels and, for comparison, on the
+    vector-ALU kernel (vector_alu = 1), and fp32.  Mask: a seeded random 25%
+    of the tile pairs plus the diagonal; inputs N(0, 1) rounded to the
+    element type.  TFLOP/s counts real tokens only (F_alg)."""
+    import torch
+    from workloads import f32_to_bf16_bits
+
+    grid, heads = (21, 45, 80), 4
+    cases = [((1, 8, 16), 128, "bf16", False), ((1, 8, 16), 128, "bf16", True),
+             ((1, 8, 8), 128, "bf16", False), ((1, 8, 8), 128, "bf16", True),
+             ((2, 4, 8), 128, "bf16", False), ((1, 8, 8), 64, "bf16", False),
+             ((1, 4, 8), 128, "bf16", False), ((1, 4, 8), 128, "bf16", True),
+             ((1, 8, 16), 128, "f32", False)]
+    stream = torch.cuda.current_stream()
+    out = []
+    for tile, d, dtype, vec in cases:
+        h = sa.sparse_attn_create(heads, d, grid, tile, dtype, vector_alu=vec)
+        L = sa.sparse_attn_layout(h)
+        nT = L["tiles"]
+        rng = np.random.default_rng(seed)
+        M = (rng.random((heads, nT, nT)) < 0.25).astype(np.uint8)
+        M[:, np.arange(nT), np.arange(nT)] = 1
+        x = rng.standard_normal((heads, int(np.prod(grid)), d), dtype=np.float32)
+        xt = torch.from_numpy(f32_to_bf16_bits(x).view(np.int16) if dtype == "bf16" else x).cuda()
+        mb = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
+        sa.sparse_attn_set_mask(h, mb, bitmap=torch.from_numpy(M).cuda())
+        ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(xt)
+        sa.sparse_attn_permute_kv(h, xt, xt, ws)
+        sa.sparse_attn_attend_raster(h, xt, o, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sa.sparse_attn_attend_raster(h, xt, o, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nt, ny, nx = L["tile_grid"]
+        c = np.array([min(tile[0], grid[0] - a * tile[0]) * min(tile[1], grid[1] - b * tile[1])
+                      * min(tile[2], grid[2] - e * tile[2])
+                      for a in range(nt) for b in range(ny) for e in range(nx)], dtype=np.float64)
+        F = 4.0 * d * sum(float(c @ M[hh].astype(np.float64) @ c) for hh in range(heads))
+        out.append({"tile": list(tile), "tile_volume": L["tile_volume"], "slot_stride": L["slot_stride"],
+                    "head_dim": d, "dtype": dtype,
+                    "kernel": "matrix cores" if L["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16 else "vector ALU",
+                    "attention_ms": ms, "tflops": F / (ms * 1e-3) / 1e12})
+        del ws, mb, o, xt
+        sa.sparse_attn_destroy(h)
+    return {"grid": list(grid), "heads": heads, "mask": "random 25% of tile pairs + diagonal", "seed": seed,
+            "reps": reps, "cases": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -258,6 +313,11 @@ def main():
                     help="skip the tile-box / Hilbert-order top-k comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (counter calibration runs)")
+    ap.add_argument("--pairing", default="auto", choices=["auto", "overlap", "all", "none"],
+                    help="work split of the matrix-core path (sparse_attn_config.pairing)")
+    ap.add_argument("--tile-sweep", action="store_true",
+                    help="instead of the step, time the attention stage over tile volumes and kernels "
+                         "and print that as the one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -269,13 +329,16 @@ def main():
     from workloads import make_workload, ones_bitmap
 
     torch.cuda.set_device(0)
+    if args.tile_sweep:
+        print(json.dumps({"tile_volume_sweep": tile_volume_sweep(sa), "env": env_info()}))
+        return
     wl = make_workload(args.workload)
     cfg = wl.config
     info = wl.info
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
     q, k, v = t(wl.q), t(wl.k), t(wl.v)
     o = torch.empty_like(q)
-    h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, wl.dtype)
+    h = sa.sparse_attn_create(wl.heads, wl.head_dim, wl.grid, wl.tile, wl.dtype, pairing=args.pairing)
     ws = torch.empty(sa.sparse_attn_workspace_bytes(h), dtype=torch.uint8, device="cuda")
     mask_buf = torch.empty(sa.sparse_attn_mask_bytes(h, info["nnz"]), dtype=torch.uint8, device="cuda")
     dense_buf = torch.empty(sa.sparse_attn_mask_bytes(h), dtype=torch.uint8, device="cuda")
@@ -418,7 +481,8 @@ def main():
     in_bytes = heads * N * d * elem
     slot_bytes = heads * sa.sparse_attn_layout(h)["slots"] * d * elem
     perm_bytes = 2 * (in_bytes + slot_bytes)  # K and V: raster read, tile-major written
-    traffic = traffic_per_launch(args.workload)
+    # The counter profile is taken with the default work split.
+    traffic = traffic_per_launch(args.workload) if args.pairing == "auto" else None
     result = {
         "metric": METRIC,
         "value": F / (ms_per_step * 1e-3) / 1e12,
@@ -436,6 +500,7 @@ def main():
                    "grid": list(cfg.grid), "tile": list(cfg.tile), "tokens": N,
                    "tile_density": round(info["tile_density"], 5),
                    "token_density": round(info["token_density"], 5),
+                   "pairing": args.pairing,
                    "step": "mask compile + permute K, V + block-sparse attention (Q read and O "
                            "written in raster order by the attention kernels)",
                    "inputs": input_fingerprint(wl)},

@@ -214,13 +214,12 @@ struct MaskBuffers {
 // kernel (it writes zeros).
 constexpr int kPairNum = 7, kPairDen = 10;
 
-// SPARSE_ATTN_PAIRING_AUTO: a layout with at most kAllPairsMax query-tile
-// pairs over all heads (a few per compute unit) sends every pair to the
-// pair kernel, whatever the overlap of its two lists: with so little work
-// the GPU is not filled, and the rows a separate row-kernel launch would
-// take (often the longest) would run after the pair kernel, on the critical
-// path.
-constexpr long long kAllPairsMax = 1024;
+// SPARSE_ATTN_PAIRING_AUTO: a layout with at most kSmallLayoutPairs
+// query-tile pairs over all heads (a few per compute unit) sends every tile
+// to the row kernel.  With so little work the GPU is not filled, and the
+// row kernel's one-tile workgroups, two per compute unit, balance it better
+// than pairs of tiles: more, shorter work items, and no union of two lists.
+constexpr long long kSmallLayoutPairs = 1024;
 
 constexpr int kMaskChunk = 256;  // rows per chunk of the order sort
 

@@ -315,8 +315,8 @@ int pairing_of(const sparse_attn_handle *h)
         return -1;
     if (h->cfg.pairing != SPARSE_ATTN_PAIRING_AUTO)
         return h->cfg.pairing;
-    return (long long)h->L.heads * h->L.nP <= sa::kAllPairsMax ? SPARSE_ATTN_PAIRING_ALL
-                                                              : SPARSE_ATTN_PAIRING_OVERLAP;
+    return (long long)h->L.heads * h->L.nP <= sa::kSmallLayoutPairs ? SPARSE_ATTN_PAIRING_NONE
+                                                                   : SPARSE_ATTN_PAIRING_OVERLAP;
 }
 
 // Scratch of sparse_attn_forward_noalloc: the permuted K and V live in this

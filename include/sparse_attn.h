@@ -126,10 +126,10 @@ enum { SPARSE_ATTN_ORDER_TILES = 0, SPARSE_ATTN_ORDER_HILBERT = 1 };
  * tiles per workgroup over the union of their key lists; the row kernel runs
  * one query tile per workgroup.  This is the library's own work split (the
  * pages define only the per-tile mask); results are the same either way.
- *   AUTO    (0): ALL when the layout has at most 1024 pairs over all heads
- *                (too little work to fill the GPU, and a second launch for
- *                single tiles would put their rows on the critical path),
- *                otherwise OVERLAP.
+ *   AUTO    (0): NONE when the layout has at most 1024 pairs over all
+ *                heads (too little work to fill the GPU: one-tile work
+ *                items, two per compute unit, balance it best), otherwise
+ *                OVERLAP.
  *   OVERLAP (1): a pair goes to the pair kernel when the union of its two
  *                lists is at most 7/10 of their total length (and when both
  *                are empty); its tiles go to the row kernel otherwise.

@@ -114,7 +114,7 @@ def _forward(h, q, k, v, M, lse=True, stages=False):
     ((3, 10, 12), (1, 4, 8), 64, "bf16"),     # 32-token tiles in 128-slot blocks
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
 ])
-@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "all"])  # auto is NONE on these grids
 def test_forward_and_lse_match_the_oracle(grid, tile, d, dtype, pairing):
     heads = 3
     N = int(np.prod(grid))

@@ -113,7 +113,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
-@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "all"])  # auto is NONE on these grids
 def test_fused_forward_equals_three_stages(grid, tile, d, dtype, pairing):
     c = _random_inputs(grid, tile, d, dtype)
     c.pairing = pairing
@@ -128,7 +128,7 @@ def test_fused_forward_equals_three_stages(grid, tile, d, dtype, pairing):
 
 
 @pytest.mark.parametrize("grid,tile,d,dtype", SHAPES)
-@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "all"])  # auto is NONE on these grids
 def test_lse_matches_the_oracle(grid, tile, d, dtype, pairing):
     c = _random_inputs(grid, tile, d, dtype)
     c.pairing = pairing

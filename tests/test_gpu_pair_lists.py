@@ -8,7 +8,7 @@ documents: tiles (2c, 2c + 1) along the pair axis form pair c; the list of a
 pair the pair kernel serves is the ascending union of its tiles' rows, each
 entry j | c_j << 16 | keep bits << 24; under the OVERLAP pairing a pair is
 served when 10 |union| <= 7 (|row 1| + |row 2|), under ALL always, under
-NONE never (AUTO: ALL for layouts of at most 1024 pairs over all heads,
+NONE never (AUTO: NONE for layouts of at most 1024 pairs over all heads,
 else OVERLAP); a pair not served has an empty list; the work order sorts
 pairs by decreasing list length, ties by pair id."""
 
@@ -53,7 +53,7 @@ def _expected(M, L, counts, mode):
     pairs = _tile_pairs(L)
     P = len(pairs)
     want_pairing = mode if mode != sa.SPARSE_ATTN_PAIRING_AUTO else (
-        sa.SPARSE_ATTN_PAIRING_ALL if heads * P <= 1024 else sa.SPARSE_ATTN_PAIRING_OVERLAP)
+        sa.SPARSE_ATTN_PAIRING_NONE if heads * P <= 1024 else sa.SPARSE_ATTN_PAIRING_OVERLAP)
     assert L["pairing"] == want_pairing
     lens, flags, lists = [], [], []
     for h in range(heads):
@@ -112,11 +112,13 @@ def test_workload_pair_lists_bit_exact(name):
     wl = make_workload(name, heads=heads, masks_only=True)
     print(f"pair lists {name} heads={wl.heads} grid={wl.grid}", flush=True)
     M = oracle.mask_of(wl)
-    h = sa.sparse_attn_create(wl.heads, 128, wl.grid, wl.tile, "bf16")
+    # OVERLAP, the split AUTO takes at full size (Small alone would run as NONE)
+    h = sa.sparse_attn_create(wl.heads, 128, wl.grid, wl.tile, "bf16", pairing="overlap")
+    mode = sa.SPARSE_ATTN_PAIRING_OVERLAP
     if wl.mask_kind == "bitmap":
-        flags = _check(h, M, wl.grid, wl.tile, bitmap=wl.bitmap)
+        flags = _check(h, M, wl.grid, wl.tile, mode, bitmap=wl.bitmap)
     else:
-        flags = _check(h, M, wl.grid, wl.tile, groups=wl.groups, gph=wl.groups_per_head)
+        flags = _check(h, M, wl.grid, wl.tile, mode, groups=wl.groups, gph=wl.groups_per_head)
     print(f"  pairs served by the pair kernel: {flags.mean():.3f}", flush=True)
 
 
@@ -134,7 +136,7 @@ PAIR_GRIDS = [
 
 @pytest.mark.parametrize("grid,tile", PAIR_GRIDS)
 @pytest.mark.parametrize("density", [0.0, 0.3, 1.0])
-@pytest.mark.parametrize("pairing", ["auto", "overlap", "none"])
+@pytest.mark.parametrize("pairing", ["auto", "overlap", "all"])  # auto is NONE on these grids
 def test_random_bitmap_pair_lists_bit_exact(grid, tile, density, pairing):
     heads = 3
     nT = oracle.num_tiles(grid, tile)

@@ -32,7 +32,8 @@ def test_compiled_workload_masks_validate(name):
 
 def test_hilbert_lists_validate_and_a_corrupted_pair_list_is_reported():
     grid, tile, heads = (3, 17, 33), (1, 8, 16), 2
-    h = sa.sparse_attn_create(heads, 128, grid, tile, "bf16", order="hilbert")
+    # OVERLAP (a layout this small would run AUTO as NONE: no pair lists)
+    h = sa.sparse_attn_create(heads, 128, grid, tile, "bf16", order="hilbert", pairing="overlap")
     ob = torch.empty(sa.sparse_attn_order_bytes(h), dtype=torch.uint8, device="cuda")
     sa.sparse_attn_set_order(h, ob)
     L = sa.sparse_attn_layout(h)
