@@ -69,7 +69,6 @@ __device__ __forceinline__ int tile_tokens(const Layout &L, const AttnParams &P,
 // waves moves K, the second half V^T.
 template <int D>
 struct RowDma {
-    static constexpr int RCK = D / 8;                   // 16-byte chunks per K row
     static constexpr int KBLK = kStage * D * 2 / 1024;  // K blocks per stage (V^T has as many)
     static constexpr int BPW = 2 * KBLK / 4;            // blocks per wave
     static_assert(KBLK % BPW == 0, "a wave moves K blocks or V^T blocks, not both");
@@ -82,7 +81,7 @@ template <int D>
 __device__ __forceinline__ void make_row_dma(RowDma<D> &pl, const uint16_t *Kp, const uint16_t *Vt,
                                              const Layout &L, int h, int wave, int lane)
 {
-    constexpr int RCK = RowDma<D>::RCK, KBLK = RowDma<D>::KBLK, BPW = RowDma<D>::BPW;
+    constexpr int KBLK = RowDma<D>::KBLK, BPW = RowDma<D>::BPW;
     pl.is_v = wave * BPW >= KBLK;
     const char *base = pl.is_v ? (const char *)(Vt + (long long)h * L.nT * D * kTile)
                                : (const char *)(Kp + (long long)h * L.Npad * D);
@@ -91,21 +90,10 @@ __device__ __forceinline__ void make_row_dma(RowDma<D> &pl, const uint16_t *Kp, 
     // byte offset (scalar) and the lane's offset in it (vector) both fit 32
     // bits.  Word 3 is the gfx9 raw 32-bit data format.
     pl.rsrc = __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, L.Npad * D * 2, 0x00020000);
-    const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
     for (int t = 0; t < BPW; ++t) {
         const int blk = wave * BPW + t;
-        const int kb = pl.is_v ? blk - KBLK : blk;
-        const int line = 4 * kb + line_in_blk;
-        const int logical = phys ^ (line & 15);
-        if (!pl.is_v) {
-            constexpr int RPL = 16 / RCK;
-            const int row = RPL * line + logical / RCK, c = logical % RCK;
-            pl.off[t] = row * D * 2 + 16 * c;
-        } else {
-            const int dv = 2 * line + (logical >> 3), c = logical & 7;
-            pl.off[t] = dv * kTile * 2 + 16 * c;
-        }
+        pl.off[t] = pl.is_v ? vt_chunk_src(blk - KBLK, lane) : k_chunk_src<D>(blk, lane);
     }
 }
 

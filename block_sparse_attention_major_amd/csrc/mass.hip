@@ -91,7 +91,6 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
                                                            float scale_log2, float *__restrict__ mass)
 {
     constexpr int KS = D / 16;
-    constexpr int RC = D / 8;                           // 16-byte chunks per row
     constexpr int TILE = kTileRows * D * 2;             // bytes of a staged key tile
     constexpr int BLK = TILE / 1024;                    // 1 KB DMA blocks per tile
     constexpr int BPW = BLK / kWaves;                   // blocks per wave
@@ -134,17 +133,9 @@ __global__ __launch_bounds__(kThreads, 1) void mass_kernel(Layout L, const uint1
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(Kt + (long long)h * L.Npad * D), 0, L.Npad * D * 2, 0x00020000);
     int voff[BPW];
-    {
-        constexpr int RPL = 16 / RC;
-        const int line_in_blk = lane >> 4, phys = lane & 15;
 #pragma unroll
-        for (int t = 0; t < BPW; ++t) {
-            const int line = 4 * (wave * BPW + t) + line_in_blk;
-            const int logical = phys ^ (line & 15);
-            const int row = RPL * line + logical / RC, c = logical % RC;
-            voff[t] = row * D * 2 + 16 * c;
-        }
-    }
+    for (int t = 0; t < BPW; ++t)
+        voff[t] = k_chunk_src<D>(wave * BPW + t, lane);
     auto stage = [&](char *buf, int j) {
         const int soff = j * TILE;
 #pragma unroll

@@ -81,6 +81,32 @@ __device__ __forceinline__ int tile_tokens(const Layout &L, const FastDiv &div_p
     return min(L.tt, L.T - a * L.tt) * min(L.th, L.H - b * L.th) * min(L.tw, L.W - e * L.tw);
 }
 
+// Copies of K and V^T into LDS move 1 KB blocks: lane l of a
+// buffer_load ... lds writes LDS bytes 16 l .. 16 l + 15 of the block, so
+// each lane fetches the global chunk that the LDS layout puts there.
+// Block kb of K rows (D / 8 chunks per row, lds_off<D / 8>) holds 256-byte
+// lines 4 kb .. 4 kb + 3; this is the byte offset, from the first row, of
+// the K chunk lane `lane` copies for it.
+template <int D>
+__device__ __forceinline__ int k_chunk_src(int kb, int lane)
+{
+    constexpr int RC = D / 8, RPL = 16 / RC;
+    const int line = 4 * kb + (lane >> 4);
+    const int logical = (lane & 15) ^ (line & 15);
+    const int row = RPL * line + logical / RC, c = logical % RC;
+    return row * D * 2 + 16 * c;
+}
+// The same for block kb of a 64-key stage of V^T (rows of 64 keys,
+// lds_off<8>), copied from the per-tile [D][kTile] layout: the byte offset
+// from the stage's first key of feature row 0.
+__device__ __forceinline__ int vt_chunk_src(int kb, int lane)
+{
+    const int line = 4 * kb + (lane >> 4);
+    const int logical = (lane & 15) ^ (line & 15);
+    const int dv = 2 * line + (logical >> 3), c = logical & 7;
+    return dv * kTile * 2 + 16 * c;
+}
+
 // s_waitcnt on this wave's vector-memory counter only (gfx9 encoding: vmcnt
 // in bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
 template <int N>
