@@ -253,8 +253,9 @@ struct AttnParams {
     FastDiv div_row;    // nx: tiles per tile-grid row
 };
 
-// bf16 matrix-core kernels, B == 128, D in {64, 128}: the pair kernel over
-// accepted query-tile pairs, then the row kernel over the other query tiles.
+// bf16 matrix-core kernels, 128 slots per tile (tile volume <= 128), D in
+// {64, 128}: the pair kernel over accepted query-tile pairs, then the row
+// kernel over the other query tiles.
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
 hipError_t launch_attention_rows(const Layout &L, const AttnParams &p, hipStream_t s);
 // Tile selection from the tile-major Q and K: fp32 tile means into qbar,

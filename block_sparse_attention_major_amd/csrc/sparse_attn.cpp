@@ -421,7 +421,7 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
         L.H = c.grid[1];
         L.W = c.grid[2];
         // A tile larger than the grid is allowed: it is clipped like any
-        // edge tile and keeps B = tt th tw slots.
+        // edge tile (its slots per tile are set with the kernel below).
         L.tt = c.tile[0];
         L.th = c.tile[1];
         L.tw = c.tile[2];
