@@ -457,7 +457,22 @@ def main():
         sel.append((a, b))
     torch.cuda.synchronize()
     select_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
-    del sel_bitmap
+    # The same with the per-head Top-k estimate (Top-p 0.9, fixed floor of a
+    # tenth of the key tiles, the page's ratio).
+    scope_keep = torch.empty((wl.heads, nT), dtype=torch.int32, device="cuda")
+    rho, k_fixed = 0.9, -(-nT // 10)
+    sa.sparse_attn_select_scope(h, rho, k_fixed, ws, sel_bitmap, keep=scope_keep)
+    sel = []
+    for _ in range(5):
+        a, b = E(), E()
+        a.record(stream)
+        sa.sparse_attn_select_scope(h, rho, k_fixed, ws, sel_bitmap, keep=scope_keep)
+        b.record(stream)
+        sel.append((a, b))
+    torch.cuda.synchronize()
+    scope_ms = float(np.mean([a.elapsed_time(b) for a, b in sel]))
+    scope_keep_mean = float(scope_keep.double().mean())
+    del sel_bitmap, scope_keep
 
     gemm = None if args.no_gemm_reference else gemm_reference(stream)
     searched = None
@@ -532,7 +547,9 @@ def main():
         "tile_selection": {"ms": select_ms, "k_per_head": [int(x) for x in kh],
                            "pool_gbs": 2 * in_bytes / (select_ms * 1e-3) / 1e9,
                            "note": "top-k over mean-pooled tile scores from the permuted Q, K; "
-                                   "not part of the timed step"},
+                                   "not part of the timed step",
+                           "per_head_estimate": {"ms": scope_ms, "rho": rho, "k_fixed": k_fixed,
+                                                 "mean_tiles_kept": scope_keep_mean}},
         "topk_by_token_order": orders,
         "window_search": searched,
         "env": env_info(),

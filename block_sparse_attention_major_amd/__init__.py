@@ -61,7 +61,8 @@ EXPORTED = [
     "sparse_attn_forward_lse", "sparse_attn_permute_kv", "sparse_attn_attend_raster",
     "sparse_attn_permute_inputs", "sparse_attn_attend", "sparse_attn_unpermute_output",
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
-    "sparse_attn_read_pair_lists", "sparse_attn_select_topk", "sparse_attn_tile_mass",
+    "sparse_attn_read_pair_lists", "sparse_attn_select_topk", "sparse_attn_select_scope",
+    "sparse_attn_tile_mass",
     "sparse_attn_search_windows",
     "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
 ]
@@ -122,6 +123,7 @@ _sigs = {
     "sparse_attn_read_index_lists": ([_vp, _vp, _vp, _i64, _vp, _vp], ctypes.c_int),
     "sparse_attn_read_pair_lists": ([_vp, _vp, _vp, _i64, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_select_topk": ([_vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    "sparse_attn_select_scope": ([_vp, ctypes.c_float, _i32, _vp, _sz, _vp, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_tile_mass": ([_vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
     "sparse_attn_search_windows": ([_vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp, _vp,
                                     _vp], ctypes.c_int),
@@ -415,6 +417,19 @@ def sparse_attn_select_topk(h, k_per_head, ws, bitmap, stream=None):
     _check(_lib.sparse_attn_select_topk(h.ptr, kh.ctypes.data, _dptr(ws, "ws"), _nbytes(ws),
                                         _sized(bitmap, "bitmap", h.sizes["bitmap"], elem=1),
                                         _stream(stream)), h)
+
+
+def sparse_attn_select_scope(h, rho, k_fixed, ws, bitmap, base=None, keep=None, stream=None):
+    """Tile bitmap with the per-head Top-k estimate from the permuted Q and K
+    in ws: per query tile the hybrid Top-p (rho) / fixed Top-k (k_fixed key
+    tiles) base count, the head's weighted estimate, then each row's
+    max(base, k_head) best key tiles.  base, keep: optional device int32
+    [heads, nT] that receive the counts."""
+    n = h.sizes["heads"] * h.sizes["tiles"] * 4
+    _check(_lib.sparse_attn_select_scope(h.ptr, float(rho), int(k_fixed), _dptr(ws, "ws"), _nbytes(ws),
+                                         _sized(bitmap, "bitmap", h.sizes["bitmap"], elem=1),
+                                         _sized(base, "base", n, elem=4), _sized(keep, "keep", n, elem=4),
+                                         _stream(stream)), h)
 
 
 def sparse_attn_read_pair_lists(h, row_ptr, cols, order, flag, stream=None):

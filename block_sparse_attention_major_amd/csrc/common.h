@@ -265,6 +265,14 @@ constexpr int kSelectMaxTiles = 8192;
 hipError_t launch_select_topk(const Layout &L, int elem_bytes, const void *q, const void *k,
                               const int *kh, float scale, float *qbar, float *kbar, uint8_t *bitmap,
                               hipStream_t s);
+// The same with the per-head Top-k estimate: per row the hybrid Top-p /
+// fixed Top-k base count into base [heads][nT] (rho: Top-p threshold,
+// k_fixed: the fixed count), the per-head estimate and final counts
+// max(base, k_head) into keep [heads][nT], then per row its keep best key
+// tiles into bitmap.
+hipError_t launch_select_scope(const Layout &L, int elem_bytes, const void *q, const void *k, float scale,
+                               float rho, int k_fixed, float *qbar, float *kbar, int *base, int *keep,
+                               uint8_t *bitmap, hipStream_t s);
 
 // Full-attention mass per tile pair from the tile-major bf16 Q and K (B ==
 // 128): mass [heads][nT][nT], row (h, i) = mean over tile i's real queries

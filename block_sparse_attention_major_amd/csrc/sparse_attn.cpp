@@ -954,6 +954,50 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
     return SPARSE_ATTN_OK;
 }
 
+int sparse_attn_select_scope(sparse_attn_handle *h, float rho, int32_t k_fixed, void *ws, size_t ws_bytes,
+                             uint8_t *bitmap, int32_t *base, int32_t *keep, void *stream)
+{
+    if (check_handle(h))
+        return SPARSE_ATTN_INVALID_ARG;
+    int st;
+    if ((st = check_ws(h, ws, ws_bytes)))
+        return st;
+    const sa::Layout &L = h->L;
+    if (!bitmap)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "bitmap must be non-null");
+    if (!std::isfinite(rho))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "rho must be finite");
+    if (k_fixed < 0 || k_fixed > L.nT)
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "k_fixed = %d is outside 0..%d", k_fixed, L.nT);
+    if (L.nT > sa::kSelectMaxTiles)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "tile selection takes at most %d tiles (%d)",
+                    sa::kSelectMaxTiles, L.nT);
+    // Scratch in the output region: tile means of Q and K (fp32), then the
+    // base and final counts (when the caller passes no arrays for them).
+    const WsLayout w = ws_layout(h);
+    const size_t means = sa::align256(size_t(L.heads) * L.nT * L.D * 4);
+    const size_t counts = sa::align256(size_t(L.heads) * L.nT * 4);
+    if (2 * means + 2 * counts > w.total - w.o)
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "tiles of %d slots are too small for the selection scratch",
+                    L.S);
+    const size_t bm = size_t(L.heads) * L.nT * L.nT, nc = size_t(L.heads) * L.nT * 4;
+    if (overlaps(bitmap, bm, ws, w.total) || (base && overlaps(base, nc, ws, w.total)) ||
+        (keep && overlaps(keep, nc, ws, w.total)) || (base && overlaps(base, nc, bitmap, bm)) ||
+        (keep && overlaps(keep, nc, bitmap, bm)) || (base && keep && overlaps(base, nc, keep, nc)))
+        return fail(h, SPARSE_ATTN_INVALID_ARG, "bitmap, base, keep and the workspace must not overlap");
+    char *b = static_cast<char *>(ws);
+    float *qbar = reinterpret_cast<float *>(b + w.o);
+    float *kbar = reinterpret_cast<float *>(b + w.o + means);
+    int *bs = base ? base : reinterpret_cast<int *>(b + w.o + 2 * means);
+    int *kp = keep ? keep : reinterpret_cast<int *>(b + w.o + 2 * means + counts);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = sa::launch_select_scope(L, h->elem_bytes, b + w.q, b + w.k, h->scale, rho, k_fixed, qbar,
+                                           kbar, bs, kp, bitmap, s);
+    if (e != hipSuccess)
+        return hip_fail(h, e, "tile selection");
+    return SPARSE_ATTN_OK;
+}
+
 int sparse_attn_permute(sparse_attn_handle *h, const void *src, void *dst, int32_t layout,
                         void *stream)
 {

@@ -372,6 +372,35 @@ int sparse_attn_select_topk(sparse_attn_handle *h, const int32_t *k_per_head, vo
                             size_t ws_bytes, uint8_t *bitmap, void *stream);
 
 /*
+ * Tile selection with the online per-head Top-k estimate (SCOPE review
+ * page, "What carries the argument" and the summary: a hybrid Top-p /
+ * fixed Top-k count per query cluster, the head's query-size-weighted
+ * average k_head = ceil(sum_c n_c b_c / sum_c n_c), and r_c =
+ * max(b_c, k_head); the page's fixed Top-k ratio is 0.1 and its Top-p
+ * threshold is not reported).  A query cluster is a query tile here, n_c
+ * its real tokens, and the proxy logits are the tile scores of
+ * sparse_attn_select_topk.  Per query tile i of head h:
+ *   p_i    = the smallest m such that the m largest softmax probabilities
+ *            of row i's scores (softmax over all key tiles) sum to at least
+ *            rho; 0 when rho <= 0, nT when rho >= 1;
+ *   base_i = min(nT, max(p_i, k_fixed));
+ *   keep_i = max(base_i, k_head), k_head = ceil(sum_i c_i base_i / N);
+ * and row i keeps its keep_i highest-scoring key tiles, ties to the lower
+ * j.  rho is applied in fp32 (row sums of fp32 exponentials), the counts
+ * are exact integers.  k_fixed: the fixed Top-k floor in key tiles (the
+ * page's ratio 0.1 is k_fixed = ceil(0.1 nT)).  Reads the permuted Q and K
+ * in ws (call sparse_attn_permute_inputs first) and uses the output region
+ * of ws as scratch.  bitmap: device uint8 [heads][nT][nT], out.  base,
+ * keep: device int32 [heads][nT], out, or NULL.  None of bitmap, base, keep
+ * may overlap ws or each other.
+ * Errors: INVALID_ARG (null bitmap, rho not finite, k_fixed outside 0..nT,
+ * overlapping buffers), UNSUPPORTED (more than 8192 tiles, or tiles too
+ * small for the scratch), WORKSPACE_TOO_SMALL, HIP_ERROR.
+ */
+int sparse_attn_select_scope(sparse_attn_handle *h, float rho, int32_t k_fixed, void *ws, size_t ws_bytes,
+                             uint8_t *bitmap, int32_t *base, int32_t *keep, void *stream);
+
+/*
  * Reference attention mass per tile pair, the input of the offline window
  * search (Compact Attention page, Fig. 1 caption: reference attention mass
  * of query-key regions; Fig. 4 caption: the search keeps the regions that

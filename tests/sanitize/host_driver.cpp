@@ -24,6 +24,8 @@ hipError_t launch_attention_mfma(const Layout &, const AttnParams &, hipStream_t
 hipError_t launch_attention_rows(const Layout &, const AttnParams &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_select_topk(const Layout &, int, const void *, const void *, const int *, float, float *, float *,
                               uint8_t *, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_select_scope(const Layout &, int, const void *, const void *, float, float, int, float *, float *,
+                               int *, int *, uint8_t *, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_tile_mass(const Layout &, const void *, const void *, float, float *, hipStream_t)
 {
     return hipErrorNotSupported;
