@@ -246,8 +246,8 @@ def gemm_reference(stream, n=16384, reps=5):
 
 def tile_volume_sweep(sa, seed=1, reps=5):
     """Attention stage of layouts of several tile volumes on the Wan grid
-    (4 heads), bf16 on the matrix-core kernels and, for comparison, on the
-    vector-ALU kernel (vector_alu = 1), and fp32.  Mask: a seeded random 25%
+    (4 heads), bf16 and fp32 on the matrix-core kernels and, for comparison,
+    on the vector-ALU kernel (vector_alu = 1).  Mask: a seeded random 25%
     of the tile pairs plus the diagonal; inputs N(0, 1) rounded to the
     element type.  TFLOP/s counts real tokens only (F_alg)."""
     import torch
@@ -258,7 +258,8 @@ def tile_volume_sweep(sa, seed=1, reps=5):
              ((1, 8, 8), 128, "bf16", False), ((1, 8, 8), 128, "bf16", True),
              ((2, 4, 8), 128, "bf16", False), ((1, 8, 8), 64, "bf16", False),
              ((1, 4, 8), 128, "bf16", False), ((1, 4, 8), 128, "bf16", True),
-             ((1, 8, 16), 128, "f32", False)]
+             ((1, 8, 16), 128, "f32", False), ((1, 8, 16), 128, "f32", True),
+             ((1, 8, 8), 128, "f32", False), ((1, 8, 16), 64, "f32", False)]
     stream = torch.cuda.current_stream()
     out = []
     for tile, d, dtype, vec in cases:
@@ -291,7 +292,7 @@ def tile_volume_sweep(sa, seed=1, reps=5):
         F = 4.0 * d * sum(float(c @ M[hh].astype(np.float64) @ c) for hh in range(heads))
         out.append({"tile": list(tile), "tile_volume": L["tile_volume"], "slot_stride": L["slot_stride"],
                     "head_dim": d, "dtype": dtype,
-                    "kernel": "matrix cores" if L["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16 else "vector ALU",
+                    "kernel": "vector ALU" if L["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC else "matrix cores",
                     "attention_ms": ms, "tflops": F / (ms * 1e-3) / 1e12})
         del ws, mb, o, xt
         sa.sparse_attn_destroy(h)

@@ -52,6 +52,7 @@ SPARSE_ATTN_LAYOUT_ROWS = 0
 SPARSE_ATTN_LAYOUT_TILE_COLUMNS = 1
 SPARSE_ATTN_KERNEL_MFMA_BF16 = 0
 SPARSE_ATTN_KERNEL_GENERIC = 1
+SPARSE_ATTN_KERNEL_MFMA_F32 = 2
 SPARSE_ATTN_MAX_GROUPS = 8
 
 EXPORTED = [
@@ -254,8 +255,8 @@ def sparse_attn_create(heads, head_dim, grid, tile, dtype, softmax_scale=0.0,
                        vector_alu=False):
     """dtype: "bf16"/"f32" or SPARSE_ATTN_BF16/SPARSE_ATTN_F32; order:
     "tiles"/"hilbert" or SPARSE_ATTN_ORDER_*; pairing: "auto"/"overlap"/
-    "all"/"none" or SPARSE_ATTN_PAIRING_*; vector_alu: run bf16 on the
-    vector-ALU kernel instead of the matrix-core kernels."""
+    "all"/"none" or SPARSE_ATTN_PAIRING_*; vector_alu: run on the vector-ALU
+    kernel instead of the matrix-core kernels."""
     if isinstance(dtype, str):
         dtype = {"bf16": SPARSE_ATTN_BF16, "f32": SPARSE_ATTN_F32}[dtype]
     if isinstance(order, str):

@@ -258,6 +258,9 @@ struct AttnParams {
 // kernel over the other query tiles.
 hipError_t launch_attention_mfma(const Layout &L, const AttnParams &p, hipStream_t s);
 hipError_t launch_attention_rows(const Layout &L, const AttnParams &p, hipStream_t s);
+// fp32 matrix-core kernel (one query tile per workgroup over the row lists),
+// D in {64, 128}; needs N_pad D 4 bytes per head below 2^31.
+hipError_t launch_attention_f32(const Layout &L, const AttnParams &p, hipStream_t s);
 // Tile selection from the tile-major Q and K: fp32 tile means into qbar,
 // kbar ([heads][nT][D]), then per row the kh[h] best-scoring key tiles
 // (ties to the lower tile) into bitmap [heads][nT][nT].  nT <= kSelectMaxTiles.

@@ -291,6 +291,8 @@ sa::AttnParams attn_params(const sparse_attn_handle *h, void *ws)
 
 hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p, hipStream_t s)
 {
+    if (h->kernel == SPARSE_ATTN_KERNEL_MFMA_F32)
+        return sa::launch_attention_f32(h->L, p, s);
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
         return sa::launch_attention_generic(h->L, h->elem_bytes, p, s);
     // The pair kernel skips pairs it does not serve and the row kernel
@@ -446,11 +448,16 @@ int sparse_attn_create(const sparse_attn_config *cfg, sparse_attn_handle **out)
     if (nT * nT * c.heads >= (1ll << 31))
         return fail(nullptr, SPARSE_ATTN_UNSUPPORTED,
                     "heads * tiles^2 = %lld does not fit 32-bit index lists", nT * nT * c.heads);
-    // bf16 runs on the matrix-core kernels, whose blocks are 128 slots for
-    // any tile volume (a smaller tile leaves slots empty); fp32, or bf16 on
-    // request, runs on the vector-ALU kernel with B slots per tile.
-    const int kernel = (c.dtype == SPARSE_ATTN_BF16 && !c.vector_alu) ? SPARSE_ATTN_KERNEL_MFMA_BF16
-                                                                     : SPARSE_ATTN_KERNEL_GENERIC;
+    // bf16 runs on the bf16 matrix-core kernels, whose blocks are 128 slots
+    // for any tile volume (a smaller tile leaves slots empty); fp32 on the
+    // fp32 matrix-core kernel, B slots per tile, while a head's rows fit its
+    // 32-bit buffer offsets; the vector-ALU kernel (B slots per tile) takes
+    // the rest and every layout on request.
+    int kernel = SPARSE_ATTN_KERNEL_GENERIC;
+    if (!c.vector_alu && c.dtype == SPARSE_ATTN_BF16)
+        kernel = SPARSE_ATTN_KERNEL_MFMA_BF16;
+    else if (!c.vector_alu && nT * B * c.head_dim * 4 < (1ll << 31))
+        kernel = SPARSE_ATTN_KERNEL_MFMA_F32;
     L.nT = (int)nT;
     L.S = kernel == SPARSE_ATTN_KERNEL_MFMA_BF16 ? 128 : (int)B;
     L.heads = c.heads;

@@ -89,9 +89,14 @@ enum {
      * 128; every tile takes S = 128 slots (a tile of B < 128 tokens leaves
      * 128 - B of them empty, and that share of the matrix work idle). */
     SPARSE_ATTN_KERNEL_MFMA_BF16 = 0,
-    /* vector-ALU kernel: fp32 always, bf16 on request
-     * (sparse_attn_config.vector_alu); S = B slots per tile. */
-    SPARSE_ATTN_KERNEL_GENERIC = 1
+    /* vector-ALU kernel, fp32 arithmetic: on request
+     * (sparse_attn_config.vector_alu), and for fp32 layouts too large for
+     * the fp32 matrix-core kernel; S = B slots per tile. */
+    SPARSE_ATTN_KERNEL_GENERIC = 1,
+    /* fp32 matrix-core kernel (v_mfma_f32_32x32x2_f32): fp32 inputs, head_dim
+     * 64 or 128, S = B slots per tile, while one head's tile-major rows
+     * (nT B head_dim 4 bytes) stay below 2^31 bytes. */
+    SPARSE_ATTN_KERNEL_MFMA_F32 = 2
 };
 
 /*
@@ -153,8 +158,8 @@ typedef struct sparse_attn_config {
     float softmax_scale;   /* score scale s; 0 selects 1 / sqrt(head_dim) */
     int32_t order;         /* SPARSE_ATTN_ORDER_TILES (0) or SPARSE_ATTN_ORDER_HILBERT */
     int32_t pairing;       /* SPARSE_ATTN_PAIRING_* (0 = AUTO) */
-    /* Nonzero runs bf16 on the vector-ALU kernel instead of the matrix-core
-     * kernels (for comparison and testing); fp32 always runs there. */
+    /* Nonzero runs on the vector-ALU kernel instead of the matrix-core
+     * kernels (for comparison and testing), bf16 and fp32 alike. */
     int32_t vector_alu;
 } sparse_attn_config;
 

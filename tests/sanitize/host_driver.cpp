@@ -22,6 +22,7 @@ hipError_t launch_compile_mask(const Layout &, int, const uint8_t *, const MaskB
                                hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attention_mfma(const Layout &, const AttnParams &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_attention_rows(const Layout &, const AttnParams &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_attention_f32(const Layout &, const AttnParams &, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_select_topk(const Layout &, int, const void *, const void *, const int *, float, float *, float *,
                               uint8_t *, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_select_scope(const Layout &, int, const void *, const void *, float, float, int, float *, float *,

@@ -65,10 +65,20 @@ def test_create_and_layout(sa):
     sa.sparse_attn_destroy(h)
     tiny = sa.sparse_attn_create(2, 64, (4, 8, 8), (1, 4, 4), "f32")
     L = sa.sparse_attn_layout(tiny)
-    assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC and L["pairing"] == -1
+    assert L["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_F32 and L["pairing"] == -1
+    assert L["v_layout"] == sa.SPARSE_ATTN_LAYOUT_ROWS
     assert L["tile_volume"] == L["slot_stride"] == 16 and L["slots"] == 16 * 16
     full = sa.sparse_attn_mask_bytes(tiny)
     assert sa.sparse_attn_mask_bytes(tiny, 100) == full - 4 * (2 * 16 * 16 - 100)
+    vec = sa.sparse_attn_create(2, 64, (4, 8, 8), (1, 4, 4), "f32", vector_alu=True)
+    assert sa.sparse_attn_layout(vec)["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    # fp32 layouts whose tile-major rows of one head reach 2^31 bytes run on
+    # the vector ALUs (the fp32 matrix-core kernel addresses a head with 32
+    # bits): 33,000 tiles of 128 tokens, d = 128, are 2.16 GB per head.
+    big = sa.sparse_attn_create(1, 128, (1, 24, 16 * 11000), (1, 8, 16), "f32")
+    assert sa.sparse_attn_layout(big)["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    mid = sa.sparse_attn_create(1, 128, (1, 24, 16 * 5000), (1, 8, 16), "f32")
+    assert sa.sparse_attn_layout(mid)["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_F32
 
 
 def test_small_bf16_tiles_take_matrix_core_blocks(sa):

@@ -78,6 +78,10 @@ def full_check(c, what):
 def test_tiny_fp32():
     wl = make_workload("tiny")
     _, _, layout = full_check(Case.of(wl), "tiny")
+    assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_F32
+    c = Case.of(wl)
+    c.vector_alu = True
+    _, _, layout = full_check(c, "tiny, vector ALU")
     assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
 
 
@@ -139,7 +143,7 @@ def test_ragged_shapes_with_empty_rows(grid, tile, d, dtype, pairing):
     if dtype == "bf16":
         assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_BF16 and layout["slot_stride"] == 128
     else:
-        assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC and layout["slot_stride"] == B
+        assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_F32 and layout["slot_stride"] == B
     nT = oracle.num_tiles(grid, tile)
     # the empty row (head 0, query tile nT // 2) outputs exactly zero
     perm, _ = oracle.perm(grid, tile)
@@ -152,11 +156,12 @@ def test_ragged_shapes_with_empty_rows(grid, tile, d, dtype, pairing):
     ((3, 20, 36), (1, 8, 16), 128),
     ((3, 10, 12), (1, 4, 8), 64),
 ])
-def test_bf16_on_the_vector_alu_kernel(grid, tile, d):
-    """bf16 inputs on the vector-ALU kernel (on request), tiles of B slots."""
-    c = _random_case(grid, tile, d, "bf16")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_on_the_vector_alu_kernel(grid, tile, d, dtype):
+    """bf16 and fp32 inputs on the vector-ALU kernel (on request), tiles of B slots."""
+    c = _random_case(grid, tile, d, dtype)
     c.vector_alu = True
-    _, _, layout = full_check(c, "bf16 vector-ALU")
+    _, _, layout = full_check(c, f"{dtype} vector-ALU")
     assert layout["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
     assert layout["slot_stride"] == int(np.prod(tile))
 

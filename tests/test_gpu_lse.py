@@ -37,9 +37,9 @@ class Inputs:
 
 
 def _random_inputs(grid, tile, d, dtype, heads=3, p=0.4, seed=0):
-    """dtype "bf16-vector": bf16 on the vector-ALU kernel."""
-    vector = dtype == "bf16-vector"
-    dtype = "bf16" if vector else dtype
+    """dtype "bf16-vector" / "f32-vector": on the vector-ALU kernel."""
+    vector = dtype.endswith("-vector")
+    dtype = dtype.split("-")[0]
     N = int(np.prod(grid))
     nT = oracle.num_tiles(grid, tile)
     q, k, v = (_rand((heads, N, d), seed + s, dtype) for s in (1, 2, 3))
@@ -108,6 +108,7 @@ SHAPES = [
     ((5, 10, 12), (2, 4, 8), 128, "bf16"),    # 64-token tiles clipped along t, y and x
     ((3, 10, 12), (1, 4, 8), 64, "bf16-vector"),  # bf16 on the vector-ALU kernel
     ((3, 10, 12), (1, 4, 8), 128, "f32"),
+    ((3, 10, 12), (1, 4, 8), 128, "f32-vector"),  # fp32 on the vector-ALU kernel
     ((2, 5, 7), (2, 2, 3), 64, "f32"),
 ]
 

@@ -37,7 +37,7 @@ def _draw(i):
         if np.prod(tile) <= 128:
             break
     return dict(grid=grid, tile=tile, d=int(rng.choice([64, 128])),
-                kind=str(rng.choice(["bf16", "bf16", "bf16", "bf16-vector", "f32"])),
+                kind=str(rng.choice(["bf16", "bf16", "bf16", "bf16-vector", "f32", "f32-vector"])),
                 order=str(rng.choice(["tiles", "hilbert"])),
                 pairing=str(rng.choice(["auto", "overlap", "all", "none"])),
                 density=float(rng.choice([0.0, 0.15, 0.4, 0.7, 1.0], p=[0.05, 0.3, 0.3, 0.2, 0.15])),
@@ -48,7 +48,7 @@ def _draw(i):
 def test_random_layout(i):
     c = _draw(i)
     grid, tile, d, heads = c["grid"], c["tile"], c["d"], c["heads"]
-    dtype = "f32" if c["kind"] == "f32" else "bf16"
+    dtype = c["kind"].split("-")[0]
     print(f"random layout {i}: {c}", flush=True)
     N = int(np.prod(grid))
     B = int(np.prod(tile))
@@ -68,7 +68,7 @@ def test_random_layout(i):
     M[0, nT // 2] = 0
 
     h = sa.sparse_attn_create(heads, d, grid, tile, dtype, order=c["order"], pairing=c["pairing"],
-                              vector_alu=c["kind"] == "bf16-vector")
+                              vector_alu=c["kind"].endswith("-vector"))
     keep = []
     if c["order"] == "hilbert":
         ob = torch.empty(sa.sparse_attn_order_bytes(h), dtype=torch.uint8, device="cuda")

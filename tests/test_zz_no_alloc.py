@@ -3,7 +3,7 @@ to the library's fixed per-device scratch array) against sparse_attn_forward
 on the same inputs, bit for bit: the same kernels run on the same data,
 only the buffer holding the permuted K and V differs.  Two calls in a row,
 the second on a smaller input, then the first shape again, on the
-matrix-core path (bf16, tile volume 128), the vector-ALU path (fp32) and
+bf16 matrix-core path (tile volume 128), the fp32 matrix-core path and
 the Hilbert order."""
 
 import numpy as np
@@ -65,10 +65,10 @@ def test_noalloc_equals_forward_then_smaller_then_again(order):
     assert torch.equal(c_ws, c_na) and torch.equal(c_na, a_na)
 
 
-def test_noalloc_fp32_vector_path():
+def test_noalloc_fp32_path():
     wl = make_workload("tiny")
     h, keep = _handle(wl)
-    assert sa.sparse_attn_layout(h)["kernel"] == sa.SPARSE_ATTN_KERNEL_GENERIC
+    assert sa.sparse_attn_layout(h)["kernel"] == sa.SPARSE_ATTN_KERNEL_MFMA_F32
     q, k, v = dev(wl.q), dev(wl.k), dev(wl.v)
     o_ws, o_na = _both(h, q, k, v)
     assert torch.equal(o_ws, o_na)
