@@ -309,8 +309,8 @@ hipError_t launch_attention(const sparse_attn_handle *h, const sa::AttnParams &p
 
 size_t lse_bytes(const sparse_attn_handle *h) { return size_t(h->L.heads) * h->L.N * sizeof(float); }
 
-// The pairing in effect on the matrix-core path (AUTO resolved); -1 for the
-// vector-ALU kernel.
+// The pairing in effect on the bf16 matrix-core path (AUTO resolved); -1 for
+// the fp32 matrix-core and vector-ALU kernels.
 int pairing_of(const sparse_attn_handle *h)
 {
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
@@ -1074,7 +1074,7 @@ int sparse_attn_read_pair_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t
     if (!row_ptr || !order || !flag || (!cols && cols_capacity > 0) || cols_capacity < 0)
         return fail(h, SPARSE_ATTN_INVALID_ARG, "null destination");
     if (h->kernel != SPARSE_ATTN_KERNEL_MFMA_BF16)
-        return fail(h, SPARSE_ATTN_UNSUPPORTED, "pair lists exist for the matrix-core kernel only");
+        return fail(h, SPARSE_ATTN_UNSUPPORTED, "pair lists exist for the bf16 matrix-core kernels only");
     if (!h->has_mask)
         return fail(h, SPARSE_ATTN_NO_MASK, "no mask set");
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -140,7 +140,8 @@ enum { SPARSE_ATTN_ORDER_TILES = 0, SPARSE_ATTN_ORDER_HILBERT = 1 };
  *                are empty); its tiles go to the row kernel otherwise.
  *   ALL     (2): every pair goes to the pair kernel; no row-kernel launch.
  *   NONE    (3): every tile goes to the row kernel; no pair-kernel launch.
- * The vector-ALU kernel ignores it.
+ * The fp32 matrix-core and vector-ALU kernels ignore it (one launch of
+ * one kernel serves every query tile).
  */
 enum {
     SPARSE_ATTN_PAIRING_AUTO = 0,
@@ -214,11 +215,12 @@ typedef struct sparse_attn_layout_info {
     int64_t pairs;
     int32_t order;         /* SPARSE_ATTN_ORDER_* of the handle */
     /* The pairing in effect (OVERLAP, ALL or NONE; AUTO resolved), or -1
-     * for the vector-ALU kernel. */
+     * for the fp32 matrix-core and vector-ALU kernels. */
     int32_t pairing;
-    /* S: slots per tile in the tile-major layout, 128 for the matrix-core
-     * kernels, B for the vector-ALU kernel.  Tile tau owns slots
-     * [tau S, tau S + S); empty ones are zero in permuted inputs. */
+    /* S: slots per tile in the tile-major layout, 128 for the bf16
+     * matrix-core kernels, B for the fp32 matrix-core and vector-ALU
+     * kernels.  Tile tau owns slots [tau S, tau S + S); empty ones are zero
+     * in permuted inputs. */
     int32_t slot_stride;
 } sparse_attn_layout_info;
 
@@ -228,9 +230,10 @@ typedef struct sparse_attn_handle sparse_attn_handle;
  * Validate a configuration and plan the tile layout (host only, no device
  * call).  Tiles are numbered raster over the tile grid (t, then y, then x);
  * tiles at the far edges of a grid the tile does not divide are clipped.
- * Each tile owns S consecutive slots (S = 128 on the matrix-core kernels,
- * B = tt th tw on the vector-ALU kernel): its c real tokens fill the first c in
- * raster order over the clipped tile, the rest are empty.
+ * Each tile owns S consecutive slots (S = 128 on the bf16 matrix-core
+ * kernels, B = tt th tw on the fp32 matrix-core and vector-ALU kernels): its
+ * c real tokens fill the first c in raster order over the clipped tile, the
+ * rest are empty.
  * Errors: INVALID_ARG (null, non-positive sizes, bad dtype, order or pairing),
  * UNSUPPORTED (head_dim not 64/128, B > 128, heads * nT * nT >= 2^31,
  * N >= 2^31, a Hilbert grid side above 2^21).
@@ -245,7 +248,7 @@ void sparse_attn_destroy(sparse_attn_handle *h);
 int sparse_attn_layout(const sparse_attn_handle *h, sparse_attn_layout_info *info);
 
 /* Device bytes the compiled-mask buffer needs for at most max_nnz kept tile
- * pairs (<= 0: heads * nT * nT).  With the matrix-core kernel the buffer
+ * pairs (<= 0: heads * nT * nT).  With the bf16 matrix-core kernels the buffer
  * holds two index lists of max_nnz entries (rows and query-tile pairs, see
  * sparse_attn_set_mask), otherwise one.  Errors: INVALID_ARG. */
 int sparse_attn_mask_bytes(const sparse_attn_handle *h, int64_t max_nnz, size_t *bytes);
@@ -274,9 +277,9 @@ int sparse_attn_set_order(sparse_attn_handle *h, void *order_buf, size_t bytes, 
  * Compile a mask on the GPU into mask_buf: per query-tile row r = h nT + i
  * the kept key tiles in ascending order (row offsets by exclusive sum of row
  * lengths), and a work order of rows by decreasing length, ties by row id.
- * With the matrix-core kernel it also compiles the same lists for pairs of
- * neighbouring query tiles (union of the two rows, each entry marked with
- * the tiles that keep it), which is what that kernel walks.
+ * With the bf16 matrix-core kernels it also compiles the same lists for
+ * pairs of neighbouring query tiles (union of the two rows, each entry
+ * marked with the tiles that keep it), which is what the pair kernel walks.
  * mask_buf (device, caller-owned, at least sparse_attn_mask_bytes(max_nnz)
  * bytes) must stay alive and unmodified while forwards use the mask; calling
  * again replaces the mask.  If the mask keeps more pairs than max_nnz, the
@@ -469,12 +472,13 @@ int sparse_attn_search_windows(sparse_attn_handle *h, const float *mass,
  *   [heads nT + 1]), index list (int32, first min(nnz, cols_capacity)
  *   entries) and work order (int32 [heads nT]) into device buffers.
  * sparse_attn_read_pair_lists: the same for the query-tile pair lists of
- *   the matrix-core kernel (rows r = h * pairs + p), plus flag (int32
+ *   the bf16 matrix-core kernels (rows r = h * pairs + p), plus flag (int32
  *   [heads * pairs]: 1 when the pair kernel serves the pair, whose list is
  *   then the union of its two tiles' rows; 0 when the row kernel serves its
  *   tiles and its list is empty).  Each entry packs key tile j (bits 0-15),
  *   its real token count (bits 16-23) and whether the pair's first and
- *   second tile keep it (bits 24, 25).  UNSUPPORTED for the generic kernel.
+ *   second tile keep it (bits 24, 25).  UNSUPPORTED for the fp32
+ *   matrix-core and vector-ALU kernels.
  * sparse_attn_mask_info: synchronizes `stream`, then reports the number of
  *   kept pairs and whether the index list overflowed its capacity.
  * Errors: INVALID_ARG, NO_MASK (index lists), UNSUPPORTED, HIP_ERROR.
