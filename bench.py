@@ -244,6 +244,45 @@ def gemm_reference(stream, n=16384, reps=5):
     return {"shape": [n, n, n], "ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS}
 
 
+def mix_ceiling(sa, stream, iters=3000):
+    """The attention stage's instruction mix with nothing else in the way
+    (sparse_attn_mix_probe: per stage and wave 32 bf16 32x32x16 products with
+    operands from LDS, the kernels' online-softmax step and a barrier; no
+    copies, no key lists, no global memory traffic), in the pair kernel's
+    ping-pong (two synchronised waves per SIMD, half a step apart) and with
+    2 (the row kernel's occupancy) and 3 unsynchronised waves per SIMD.  Reported beside the
+    library GEMM as context for the attention stage's fraction of the
+    published peak: the clock, and so the rate, follows the power this work
+    draws.  mfma_busy counts 32 clocks per product (1024 FLOP per clock per
+    SIMD at the published peak) over the slowest wave's loop, which spans
+    nearly the whole launch (the waves of a SIMD do not finish together);
+    clock_ghz is that wave's s_memtime cycles over the launch's event
+    time; wave_cycles gives the spread."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = []
+    for w, pp in ((2, True), (2, False), (3, False)):
+        n = cus * w
+        cyc = torch.zeros(n * 4, dtype=torch.int64, device="cuda")
+        sink = torch.empty(n * 256, dtype=torch.float32, device="cuda")
+        sa.sparse_attn_mix_probe(w, cus, iters, cyc, sink, pingpong=pp, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        sa.sparse_attn_mix_probe(w, cus, iters, cyc, sink, pingpong=pp, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = cyc.cpu().numpy().astype(np.float64)
+        span = float(c.max())
+        tf = n * 4 * iters * 32 * 32768.0 / (ms * 1e-3) / 1e12
+        out.append({"schedule": "ping-pong (pair kernel)" if pp else "independent waves",
+                    "waves_per_simd": w, "ms": ms, "tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+                    "wave_cycles": {"min": float(c.min()), "median": float(np.median(c)), "max": span},
+                    "mfma_busy": w * 32 * 32 * iters / span, "clock_ghz": span / (ms * 1e-3) / 1e9})
+        del cyc, sink
+    return out
+
+
 def tile_volume_sweep(sa, seed=1, reps=5):
     """Attention stage of layouts of several tile volumes on the Wan grid
     (4 heads), bf16 and fp32 on the matrix-core kernels and, for comparison,
@@ -310,6 +349,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
     ap.add_argument("--no-search", action="store_true", help="skip the window-search measurement")
     ap.add_argument("--no-gemm-reference", action="store_true", help="skip the library GEMM reference")
+    ap.add_argument("--no-mix-ceiling", action="store_true",
+                    help="skip the instruction-mix probe (attention stage mix, no memory traffic)")
     ap.add_argument("--no-order-comparison", action="store_true",
                     help="skip the tile-box / Hilbert-order top-k comparison")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -319,6 +360,9 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true",
                     help="instead of the step, time the attention stage over tile volumes and kernels "
                          "and print that as the one JSON line")
+    ap.add_argument("--mix-ceiling-only", action="store_true",
+                    help="instead of the step, run only the instruction-mix probe (with the library GEMM "
+                         "reference) and print that as the one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -332,6 +376,11 @@ def main():
     torch.cuda.set_device(0)
     if args.tile_sweep:
         print(json.dumps({"tile_volume_sweep": tile_volume_sweep(sa), "env": env_info()}))
+        return
+    if args.mix_ceiling_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"mix_ceiling": mix_ceiling(sa, stream),
+                          "library_gemm_reference": gemm_reference(stream), "env": env_info()}))
         return
     wl = make_workload(args.workload)
     cfg = wl.config
@@ -476,6 +525,7 @@ def main():
     del sel_bitmap, scope_keep
 
     gemm = None if args.no_gemm_reference else gemm_reference(stream)
+    mix = None if args.no_mix_ceiling else mix_ceiling(sa, stream)
     searched = None
     if not args.no_search:
         searched = window_search(sa, wl, q, k, v, stream)
@@ -523,7 +573,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F,
-                     "library_gemm_reference": gemm},
+                     "library_gemm_reference": gemm, "mix_ceiling": mix},
         "attention": {"ms": attn_ms, "ms_median": attn_median, "ms_min": float(attn_min),
                       "tflops": attn_tflops,
                       "pct_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS,

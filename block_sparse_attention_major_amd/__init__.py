@@ -64,7 +64,7 @@ EXPORTED = [
     "sparse_attn_permute", "sparse_attn_unpermute", "sparse_attn_read_index_lists",
     "sparse_attn_read_pair_lists", "sparse_attn_select_topk", "sparse_attn_select_scope",
     "sparse_attn_tile_mass",
-    "sparse_attn_search_windows",
+    "sparse_attn_search_windows", "sparse_attn_mix_probe",
     "sparse_attn_mask_info", "sparse_attn_status_string", "sparse_attn_last_error",
 ]
 
@@ -128,6 +128,7 @@ _sigs = {
     "sparse_attn_tile_mass": ([_vp, _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
     "sparse_attn_search_windows": ([_vp, _vp, _vp, _vp, ctypes.c_double, ctypes.c_double, _vp, _vp,
                                     _vp], ctypes.c_int),
+    "sparse_attn_mix_probe": ([_i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "sparse_attn_mask_info": ([_vp, _P(_i64), _P(_i32), _vp], ctypes.c_int),
     "sparse_attn_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "sparse_attn_last_error": ([_vp], ctypes.c_char_p),
@@ -448,6 +449,20 @@ def sparse_attn_mask_info(h, stream=None):
     nnz, ovf = _i64(), _i32()
     _check(_lib.sparse_attn_mask_info(h.ptr, ctypes.byref(nnz), ctypes.byref(ovf), _stream(stream)), h)
     return nnz.value, bool(ovf.value)
+
+
+def sparse_attn_mix_probe(waves_per_simd, cus, iters, cycles, sink, pingpong=False, stream=None):
+    """Diagnostic: the attention stage's instruction mix with nothing else
+    in the way, in the row kernel's schedule (waves_per_simd unsynchronised
+    waves per SIMD) or, with pingpong (waves_per_simd 2), the pair kernel's.
+    cycles: device int64 tensor of cus * waves_per_simd * 4 elements (each
+    wave's loop cycles, out); sink: device fp32 tensor of
+    cus * waves_per_simd * 256 elements.  Asynchronous on `stream`."""
+    n = int(cus) * int(waves_per_simd)
+    cp = _sized(cycles, "cycles", n * 4 * 8, elem=8)
+    sp = _sized(sink, "sink", n * 256 * 4, elem=4)
+    _check(_lib.sparse_attn_mix_probe(int(waves_per_simd), int(bool(pingpong)), int(cus), int(iters), cp, sp,
+                                      _stream(stream)))
 
 
 class SparseAttention:

@@ -17,7 +17,7 @@ LIB = os.path.join(HERE, "libsparse_attn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["sparse_attn.cpp", "permute.hip", "mask.hip", "attn_mfma.hip", "attn_rows.hip", "attn_f32.hip",
+SOURCES = ["sparse_attn.cpp", "permute.hip", "mask.hip", "attn_mfma.hip", "attn_rows.hip", "attn_f32.hip", "mix_probe.hip",
            "attn_generic.hip", "select.hip", "mass.hip", "search.cpp"]
 
 # Packed fp32 VALU instructions are switched off for every device compile.

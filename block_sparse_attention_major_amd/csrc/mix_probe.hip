@@ -1,0 +1,214 @@
+// Diagnostic: the rate at which this GPU sustains the instruction mix of one
+// attention stage when nothing else is in the way.  It is measurement
+// context for the attention kernels' fraction of the published matrix peak,
+// not part of the attention path.
+//
+// Each wave runs `iters` stages of what a wave of the row kernel does per
+// 64-key stage: S^T = K Q^T as 16 v_mfma_f32_32x32x16_bf16 products with K
+// read from LDS, the online-softmax step of the attention kernels
+// (mfma::online_softmax: scale and reference FMA, exp2, bf16 packs, v_dot2
+// row sums, the wave-uniform redo test), and O^T += V^T P^T as 16 more
+// products with V^T read from LDS, with workgroup barriers.  The LDS stage
+// is written once before the loop, so there are no copies, no key lists and
+// no global memory traffic inside it.  Two schedules:
+//  - independent: workgroups of 4 waves (one per SIMD) run W to a compute
+//    unit, so each SIMD holds W unsynchronised waves; W = 2 is the row
+//    kernel's occupancy, W = 3 one wave more than any attention kernel
+//    holds; one barrier per stage, as in the row kernel;
+//  - ping-pong: one workgroup of 8 waves per compute unit, two per SIMD, in
+//    the pair kernel's schedule: waves 4-7 pass one extra barrier first, so
+//    they run half a step behind waves 0-3, and a step is [barrier]
+//    O^T += V^T P^T (previous stage), S^T = K Q^T [barrier] softmax; while
+//    one wave of a SIMD issues products the other runs its softmax.
+//
+// Operands are pseudo-random bf16 values in [-1, 1) (an integer hash of
+// their position), so the matrix cores switch about as much as with real
+// activations; the clock, and with it the rate, depends on that power.
+#include "mix_probe.h"
+
+#include "mfma_util.h"
+
+namespace sa {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kD = 128;
+constexpr int kStageBytes = 2 * kStage * kD * 2;  // K [64][128] then V^T [128][64], bf16
+
+// A value in [-1, 1) from a 32-bit position (lowbias32 integer hash).
+__device__ __forceinline__ float hash_unit(uint32_t x)
+{
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return (float)(int32_t)x * (1.0f / 2147483648.0f);
+}
+
+template <int W>
+__global__ __launch_bounds__(256, W) void mix_kernel(int iters, long long *cycles, float *sink)
+{
+    constexpr int KS = kD / 16, NB = kD / 32, RCK = kD / 8;
+    __shared__ __attribute__((aligned(1024))) char stage[kStageBytes];
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    for (int i = tid; i < kStageBytes / 2; i += 256)
+        ((__bf16 *)stage)[i] = (__bf16)hash_unit(0x9e3779b9u * blockIdx.x + i);
+    __syncthreads();
+
+    // Q operand of this lane (query l32, features 16 ks + 8 hi .. + 7).
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            qf[ks][u] = (__bf16)hash_unit(0x85ebca6bu * (blockIdx.x * 256 + tid) + 8 * ks + u);
+    RowState<kD> st;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            st.acc[nb][jj] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)kD);
+    const char *Ks = stage, *Vs = stage + kStageBytes / 2;
+    const int prow = key_of_mfma_row(l32);
+
+    const long long t0 = (long long)__builtin_amdgcn_s_memtime();
+    for (int it = 0; it < iters; ++it) {
+        Scores S;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            S.s0[jj] = 0.f;
+            S.s1[jj] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi));
+            const bf16x8 a1 = *(const bf16x8 *)(Ks + lds_off<RCK>(32 + prow, 2 * ks + hi));
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
+            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], S.s1, 0, 0, 0);
+        }
+        Probs P;
+        online_softmax<kD>(P, S, kStage, sl2, st);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 2 * q + hi)), P.p[q], st.acc[nb], 0, 0, 0);
+        __syncthreads();
+    }
+    const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+
+    float s = st.l;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            s += st.acc[nb][jj];
+    sink[blockIdx.x * 256 + tid] = s;
+    if (lane == 0)
+        cycles[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
+}
+
+// The ping-pong schedule: 8 waves, one stage per step, two barriers a step.
+__global__ __launch_bounds__(512, 1) void mix_pingpong_kernel(int iters, long long *cycles, float *sink)
+{
+    constexpr int KS = kD / 16, NB = kD / 32, RCK = kD / 8;
+    __shared__ __attribute__((aligned(1024))) char stage[kStageBytes];
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+    const int group = __builtin_amdgcn_readfirstlane(tid >> 8);
+    for (int i = tid; i < kStageBytes / 2; i += 512)
+        ((__bf16 *)stage)[i] = (__bf16)hash_unit(0x9e3779b9u * blockIdx.x + i);
+    __syncthreads();
+
+    bf16x8 qf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            qf[ks][u] = (__bf16)hash_unit(0x85ebca6bu * (blockIdx.x * 512 + tid) + 8 * ks + u);
+    RowState<kD> st;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            st.acc[nb][jj] = 0.f;
+    st.m = -INFINITY;
+    st.l = 0.f;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)kD);
+    const char *Ks = stage, *Vs = stage + kStageBytes / 2;
+    const int prow = key_of_mfma_row(l32);
+    Probs P;
+    auto pv = [&]() {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    *(const bf16x8 *)(Vs + lds_off<8>(32 * nb + l32, 2 * q + hi)), P.p[q], st.acc[nb], 0, 0, 0);
+    };
+
+    const long long t0 = (long long)__builtin_amdgcn_s_memtime();
+    if (group == 1)
+        lds_barrier();  // half a step behind group 0
+    for (int it = 0; it < iters; ++it) {
+        lds_barrier();
+        if (it > 0)
+            pv();
+        Scores S;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            S.s0[jj] = 0.f;
+            S.s1[jj] = 0.f;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a0 = *(const bf16x8 *)(Ks + lds_off<RCK>(prow, 2 * ks + hi));
+            const bf16x8 a1 = *(const bf16x8 *)(Ks + lds_off<RCK>(32 + prow, 2 * ks + hi));
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], S.s0, 0, 0, 0);
+            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], S.s1, 0, 0, 0);
+        }
+        lds_barrier();
+        online_softmax<kD>(P, S, kStage, sl2, st);
+    }
+    if (group == 0)
+        lds_barrier();  // every wave passes 2 iters + 1 barriers
+    pv();
+    const long long t1 = (long long)__builtin_amdgcn_s_memtime();
+
+    float s = st.l;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            s += st.acc[nb][jj];
+    sink[blockIdx.x * 512 + tid] = s;
+    if (lane == 0)
+        cycles[blockIdx.x * 8 + (tid >> 6)] = t1 - t0;
+}
+
+}  // namespace
+
+hipError_t launch_mix_probe(int waves_per_simd, int pingpong, int cus, int iters, long long *cycles, float *sink,
+                            hipStream_t s)
+{
+    if (pingpong) {
+        hipLaunchKernelGGL(mix_pingpong_kernel, dim3(cus), dim3(512), 0, s, iters, cycles, sink);
+        return hipGetLastError();
+    }
+    const dim3 grid(cus * waves_per_simd), block(256);
+    if (waves_per_simd == 1)
+        hipLaunchKernelGGL(mix_kernel<1>, grid, block, 0, s, iters, cycles, sink);
+    else if (waves_per_simd == 2)
+        hipLaunchKernelGGL(mix_kernel<2>, grid, block, 0, s, iters, cycles, sink);
+    else
+        hipLaunchKernelGGL(mix_kernel<3>, grid, block, 0, s, iters, cycles, sink);
+    return hipGetLastError();
+}
+
+}  // namespace sa

@@ -14,6 +14,7 @@
 #include <vector>
 
 #include "common.h"
+#include "mix_probe.h"
 
 struct sparse_attn_handle {
     sparse_attn_config cfg;
@@ -1113,3 +1114,20 @@ int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow
 }
 
 }  // extern "C"
+
+int sparse_attn_mix_probe(int32_t waves_per_simd, int32_t pingpong, int32_t cus, int32_t iters, int64_t *cycles,
+                          float *sink, void *stream)
+{
+    if (waves_per_simd < 1 || waves_per_simd > 3)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "waves_per_simd must be 1, 2 or 3");
+    if (pingpong != 0 && (pingpong != 1 || waves_per_simd != 2))
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "pingpong must be 0, or 1 with waves_per_simd 2");
+    if (cus < 1 || cus > 65536 || iters < 1 || iters > (1 << 24))
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cus must be in 1..65536 and iters in 1..2^24");
+    if (!cycles || !sink || reinterpret_cast<uintptr_t>(cycles) % 8 || reinterpret_cast<uintptr_t>(sink) % 4)
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cycles and sink must be non-null and aligned");
+    const hipError_t e = sa::launch_mix_probe(waves_per_simd, pingpong, cus, iters,
+                                              reinterpret_cast<long long *>(cycles), sink,
+                                              static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SPARSE_ATTN_OK : hip_fail(nullptr, e, "mix probe launch");
+}

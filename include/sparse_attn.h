@@ -492,6 +492,35 @@ int sparse_attn_read_pair_lists(sparse_attn_handle *h, int32_t *row_ptr, int32_t
                                 int64_t cols_capacity, int32_t *order, int32_t *flag, void *stream);
 int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow, void *stream);
 
+/*
+ * Diagnostic, not part of the attention path: how fast this GPU runs the
+ * instruction mix of one attention stage with nothing else in the way, as
+ * context for the attention kernels' fraction of the published matrix peak
+ * (the chip's clock, and so its rate, follows the power that work draws).
+ * Each wave runs `iters` stages of an attention wave's work on a 64-key
+ * stage held in LDS: 16 v_mfma_f32_32x32x16_bf16 products of S^T = K Q^T,
+ * the kernels' online-softmax step on the 32 x 64 scores, 16 products of
+ * O^T += V^T P^T, and workgroup barriers; head_dim 128, operands
+ * pseudo-random bf16 in [-1, 1), no global memory traffic inside the loop.
+ * One stage of one wave is 32 products of 32 x 32 x 16, 2^20 FLOP.
+ *   pingpong 0: cus * waves_per_simd workgroups of 4 waves (one per SIMD),
+ *     waves_per_simd of them resident per compute unit when cus is the
+ *     GPU's compute-unit count; the waves of a SIMD run unsynchronised, one
+ *     barrier per stage (the row kernel's schedule at waves_per_simd 2);
+ *   pingpong 1 (waves_per_simd must be 2): cus workgroups of 8 waves, two
+ *     per SIMD, waves 4-7 half a step behind waves 0-3 through one extra
+ *     barrier, two barriers per stage (the pair kernel's schedule).
+ *   waves_per_simd: 1, 2 or 3; cus: 1..65536; iters: 1..2^24;
+ *   cycles: device int64 [cus * waves_per_simd * 4], out: each wave's
+ *     shader-clock cycles over its loop (s_memtime);
+ *   sink: device fp32 [cus * waves_per_simd * 256], out: a per-lane sum of
+ *     the results (keeps the work live; its value means nothing).
+ * Asynchronous on `stream`.  Errors: INVALID_ARG, HIP_ERROR (message in
+ * sparse_attn_last_error(NULL)).
+ */
+int sparse_attn_mix_probe(int32_t waves_per_simd, int32_t pingpong, int32_t cus, int32_t iters, int64_t *cycles,
+                          float *sink, void *stream);
+
 /* Static description of a status code. */
 const char *sparse_attn_status_string(int status);
 

@@ -13,6 +13,7 @@
 
 #include "sparse_attn.h"
 #include "common.h"
+#include "mix_probe.h"
 
 namespace sa {
 hipError_t launch_permute_rows(const Layout &, int, const void *, void *, hipStream_t) { return hipErrorNotSupported; }
@@ -32,6 +33,7 @@ hipError_t launch_tile_mass(const Layout &, const void *, const void *, float, f
     return hipErrorNotSupported;
 }
 hipError_t launch_attention_generic(const Layout &, int, const AttnParams &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_mix_probe(int, int, int, int, long long *, float *, hipStream_t) { return hipErrorNotSupported; }
 }  // namespace sa
 
 static int g_fail = 0;

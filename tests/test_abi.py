@@ -293,3 +293,27 @@ def test_noalloc_forward_refuses_layouts_beyond_its_scratch(sa):
     ns = 12 * Ls["tokens"] * 128 * 2
     st = sa._lib.sparse_attn_forward_noalloc(small.ptr, fake, fake + ns, fake + 2 * ns, fake + 3 * ns, None)
     assert st == sa.SPARSE_ATTN_NO_MASK
+
+
+@pytest.mark.parametrize("waves,cus,iters", [(0, 256, 10), (4, 256, 10), (2, 0, 10), (2, 256, 0),
+                                             (2, 256, (1 << 24) + 1)])
+def test_mix_probe_rejects_bad_sizes(sa, waves, cus, iters):
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_mix_probe(waves, cus, iters, 1 << 20, 1 << 21, stream=0)
+    assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    assert "must" in sa.sparse_attn_last_error(None)
+
+
+def test_mix_probe_pingpong_needs_two_waves_per_simd(sa):
+    for waves in (1, 3):
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_mix_probe(waves, 256, 10, 1 << 20, 1 << 21, pingpong=True, stream=0)
+        assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
+    assert sa._lib.sparse_attn_mix_probe(2, 2, 256, 10, 1 << 20, 1 << 21, 0) == sa.SPARSE_ATTN_INVALID_ARG
+
+
+def test_mix_probe_rejects_null_or_misaligned_buffers(sa):
+    for cyc, sink in [(None, 1 << 21), (1 << 20, None), ((1 << 20) + 4, 1 << 21), (1 << 20, (1 << 21) + 2)]:
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_mix_probe(2, 256, 10, cyc, sink, stream=0)
+        assert e.value.status == sa.SPARSE_ATTN_INVALID_ARG
