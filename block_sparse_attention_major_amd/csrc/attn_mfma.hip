@@ -131,126 +131,6 @@ __device__ __forceinline__ void issue_block(const DmaPlan<D> &pl, char *Kd, char
                                              pl.off[t], soff, 0, 0);
 }
 
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
-
-// S = K Q^T for the kv real keys (1..64) of the stage whose K is at Ks; keys
-// past kv score -inf.  dma(t) issues this wave's DMA block t of a later
-// stage; the calls are spread over the products so the copies queue behind
-// matrix work instead of leaving in one burst.
-template <int D, typename Dma>
-__device__ __forceinline__ void qk_stage(Scores &S, const char *Ks, const bf16x8 (&qf)[D / 16],
-                                         const int (&kofs)[D / 16], int kv, int hi, Dma &&dma)
-{
-    constexpr int KS = D / 16;
-    constexpr int SUB1 = 64 * D;  // second 32-key half: 32 rows further on, same swizzle
-    constexpr int PER = KS / Stage<D>::BPW;
-    static_assert(PER * Stage<D>::BPW == KS, "DMA blocks must spread evenly over the k-steps");
-    const bool two = kv > 32;
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-        S.s0[jj] = 0.f;
-        S.s1[jj] = 0.f;
-    }
-    // Operands are read two k-steps ahead of the products that use them, so
-    // the LDS latency hides behind four matrix instructions.
-    if (two) {
-        bf16x8 r0[KS], r1[KS];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            r0[ks] = *(const bf16x8 *)(Ks + kofs[ks]);
-            r1[ks] = *(const bf16x8 *)(Ks + SUB1 + kofs[ks]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS) {
-                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs[ks + 2]);
-                r1[ks + 2] = *(const bf16x8 *)(Ks + SUB1 + kofs[ks + 2]);
-            }
-            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
-            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[ks], qf[ks], S.s1, 0, 0, 0);
-            if (ks % PER == PER - 1)
-                dma(ks / PER);
-        }
-        // Keep that order: reads of steps 0 and 1, then per step the reads
-        // of step ks + 2 and the products of ks.
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS)
-                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
-        }
-    } else {
-        bf16x8 r0[KS];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            r0[ks] = *(const bf16x8 *)(Ks + kofs[ks]);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS)
-                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs[ks + 2]);
-            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
-            if (ks % PER == PER - 1)
-                dma(ks / PER);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 2 < KS)
-                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        }
-    }
-    if (kv < kStage)
-        mask_stage_tail(S, kv, hi);
-}
-
-// O^T += V^T P^T over the stage whose V^T is at Vs (kv real keys).
-template <int D>
-__device__ __forceinline__ void pv_stage(const char *Vs, const int (&vofs)[4], const Probs &P, int kv,
-                                         RowState<D> &st)
-{
-    constexpr int NB = D / 32;
-    const int steps = kv > 32 ? 4 : 2;
-    // A operand = V^T rows 32 nb + l32, keys in 16-key steps (rows 32 apart
-    // are 16 swizzle lines apart: same pattern, 4 KB on).  The operands of
-    // a key step are read while the products of the previous one run.
-    bf16x8 va[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-        va[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs[0]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        if (q < steps) {
-            bf16x8 vn[NB];
-            if (q + 1 < steps) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    vn[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs[q + 1]);
-            }
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[nb], P.p[q], st.acc[nb], 0, 0, 0);
-            if (q + 1 < steps) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-                    va[nb] = vn[nb];
-            }
-        }
-    }
-    if (steps == 4) {
-        // Keep that order: reads of step q + 1, then the products of q.
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (q + 1 < 4)
-                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NB, 0);
-        }
-    }
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnParams P)
 {
@@ -478,9 +358,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
         wait_vmcnt<BPW>();
         lds_barrier();
         if (attends(dprev))
-            pv_stage<D>(Vp, vofs, Pr, dprev & 255, st);
+            pv_stage<D>(Vp, [&](int q) { return vofs[q]; }, Pr, dprev & 255, st);
         if (attends(dcur))
-            qk_stage<D>(S, Kc, qf, kofs, dcur & 255, hi, [](int) {});
+            qk_stage<D>(S, Kc, qf, [&](int ks) { return kofs[ks]; }, dcur & 255, hi);
         lds_barrier();
         int src;
         dnext = take(src);

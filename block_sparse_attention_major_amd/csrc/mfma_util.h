@@ -148,6 +148,54 @@ struct Probs {
 // stage is redone against its true maximum (see online_softmax).
 constexpr float kProbCap = 65536.0f;
 
+// Probabilities of 16-key step q (0..3) of a stage against the reference m,
+// rounded to bf16 into P.p[q]; returns ls plus their sum.  The steps are
+// summed in order, so a stage's row sum is the same however its steps are
+// split between calls.
+__device__ __forceinline__ float step_probs(Probs &P, const Scores &S, int q, float sl2, float m, float ls)
+{
+    const f32x16 &src = q < 2 ? S.s0 : S.s1;
+    const int o = (q & 1) * 8;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+        P.p[q][jj] = (__bf16)exp2_fast(fmaf(src[o + jj], sl2, -m));
+    return row_sum_bf16(P.p[q], ls);
+}
+
+// The redo of a stage whose probability sum left [0, kProbCap]: moves the
+// reference to the true running maximum, rescales the accumulator and row
+// sum, and recomputes the stage's probabilities; returns their sum.
+template <int D>
+__device__ __forceinline__ float redo_stage(Probs &P, const Scores &S, bool two, float sl2, RowState<D> &st)
+{
+    constexpr int NB = D / 32;
+    float mx = S.s0[0];
+#pragma unroll
+    for (int jj = 1; jj < 16; ++jj)
+        mx = fmaxf(mx, S.s0[jj]);
+    if (two) {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            mx = fmaxf(mx, S.s1[jj]);
+    }
+    const float t = half_max(mx) * sl2;
+    const float m_new = fmaxf(st.m, t);
+    const float alpha = exp2_fast(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj)
+            st.acc[nb][jj] *= alpha;
+    float ls = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (q < 2 || two)
+            ls = step_probs(P, S, q, sl2, st.m, ls);
+    return ls;
+}
+
 // Online softmax step over the kv real keys (1..64) of a stage: scores ->
 // bf16 probabilities, running row sum updated, accumulator rescaled when the
 // reference moves.  sl2 = softmax scale * log2(e).
@@ -164,46 +212,14 @@ constexpr float kProbCap = 65536.0f;
 template <int D>
 __device__ __forceinline__ void online_softmax(Probs &P, const Scores &S, int kv, float sl2, RowState<D> &st)
 {
-    constexpr int NB = D / 32;
     const bool two = kv > 32;
-    auto probs = [&]() {
-        float ls = 0.f;
+    float ls = 0.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            if (q < 2 || two) {
-                const f32x16 &src = q < 2 ? S.s0 : S.s1;
-                const int o = (q & 1) * 8;
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    P.p[q][jj] = (__bf16)exp2_fast(fmaf(src[o + jj], sl2, -st.m));
-                ls = row_sum_bf16(P.p[q], ls);
-            }
-        }
-        return ls;
-    };
-    float ls = probs();
-    if (__ballot(!(ls <= kProbCap))) {
-        float mx = S.s0[0];
-#pragma unroll
-        for (int jj = 1; jj < 16; ++jj)
-            mx = fmaxf(mx, S.s0[jj]);
-        if (two) {
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                mx = fmaxf(mx, S.s1[jj]);
-        }
-        const float t = half_max(mx) * sl2;
-        const float m_new = fmaxf(st.m, t);
-        const float alpha = exp2_fast(st.m - m_new);
-        st.m = m_new;
-        st.l *= alpha;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj)
-                st.acc[nb][jj] *= alpha;
-        ls = probs();
-    }
+    for (int q = 0; q < 4; ++q)
+        if (q < 2 || two)
+            ls = step_probs(P, S, q, sl2, st.m, ls);
+    if (__ballot(!(ls <= kProbCap)))
+        ls = redo_stage<D>(P, S, two, sl2, st);
     st.l += ls;
 }
 
@@ -219,6 +235,121 @@ __device__ __forceinline__ void mask_stage_tail(Scores &S, int kv, int hi)
             S.s0[jj] = -INFINITY;
         if (32 + c >= lim)
             S.s1[jj] = -INFINITY;
+    }
+}
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+// S = K Q^T for the kv real keys (1..64) of the stage whose K is at Ks;
+// kofs(ks) is the lane's operand offset for k-step ks,
+// lds_off<D / 8>(key_of_mfma_row(l32), 2 ks + hi) (which is that of k-step 0
+// XOR ks << 5).  Keys past kv score -inf.  Operands are read two k-steps
+// ahead of the products that use them, so the LDS latency hides behind four
+// matrix instructions.
+template <int D, typename KOfs>
+__device__ __forceinline__ void qk_stage(Scores &S, const char *Ks, const bf16x8 (&qf)[D / 16], KOfs &&kofs,
+                                         int kv, int hi)
+{
+    constexpr int KS = D / 16;
+    constexpr int SUB1 = 64 * D;  // second 32-key half: 32 rows further on, same swizzle
+    const bool two = kv > 32;
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+        S.s0[jj] = 0.f;
+        S.s1[jj] = 0.f;
+    }
+    if (two) {
+        bf16x8 r0[KS], r1[KS];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            r0[ks] = *(const bf16x8 *)(Ks + kofs(ks));
+            r1[ks] = *(const bf16x8 *)(Ks + SUB1 + kofs(ks));
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS) {
+                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs(ks + 2));
+                r1[ks + 2] = *(const bf16x8 *)(Ks + SUB1 + kofs(ks + 2));
+            }
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
+            S.s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[ks], qf[ks], S.s1, 0, 0, 0);
+        }
+        // Keep that order: reads of steps 0 and 1, then per step the reads
+        // of step ks + 2 and the products of ks.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 2, 0);
+        }
+    } else {
+        bf16x8 r0[KS];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            r0[ks] = *(const bf16x8 *)(Ks + kofs(ks));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS)
+                r0[ks + 2] = *(const bf16x8 *)(Ks + kofs(ks + 2));
+            S.s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[ks], qf[ks], S.s0, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 2 < KS)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        }
+    }
+    if (kv < kStage)
+        mask_stage_tail(S, kv, hi);
+}
+
+// O^T += V^T P^T over the stage whose V^T is at Vs (kv real keys); vofs(q)
+// is the lane's operand offset for 16-key step q, lds_off<8>(l32, 2 q + hi)
+// (that of step 0 XOR q << 5).  The operands of key step q + 1 are read
+// while the products of step q run.
+template <int D, typename VOfs>
+__device__ __forceinline__ void pv_stage(const char *Vs, VOfs &&vofs, const Probs &P, int kv, RowState<D> &st)
+{
+    constexpr int NB = D / 32;
+    const int steps = kv > 32 ? 4 : 2;
+    // A operand = V^T rows 32 nb + l32, keys in 16-key steps (rows 32 apart
+    // are 16 swizzle lines apart: same pattern, 4 KB on).
+    bf16x8 va[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+        va[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs(0));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (q < steps) {
+            bf16x8 vn[NB];
+            if (q + 1 < steps) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    vn[nb] = *(const bf16x8 *)(Vs + 4096 * nb + vofs(q + 1));
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+                st.acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[nb], P.p[q], st.acc[nb], 0, 0, 0);
+            if (q + 1 < steps) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    va[nb] = vn[nb];
+            }
+        }
+    }
+    if (steps == 4) {
+        // Keep that order: reads of step q + 1, then the products of q.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (q + 1 < 4)
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, NB, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, NB, 0);
+        }
     }
 }
 
