@@ -573,7 +573,10 @@ def main():
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNELS, "achieved": attn_tflops,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic, "flops_per_launch": F,
-                     "library_gemm_reference": gemm, "mix_ceiling": mix},
+                     "library_gemm_reference": gemm, "mix_ceiling": mix,
+                     # the attention stage's rate over that of the instruction-mix probe in
+                     # the pair kernel's own schedule (no copies, lists or clipped tiles)
+                     "frac_of_pingpong_mix": (attn_tflops / mix[0]["tflops"]) if mix else None},
         "attention": {"ms": attn_ms, "ms_median": attn_median, "ms_min": float(attn_min),
                       "tflops": attn_tflops,
                       "pct_peak": 100 * attn_tflops / PEAK_BF16_TFLOPS,

@@ -1122,8 +1122,8 @@ int sparse_attn_mix_probe(int32_t waves_per_simd, int32_t pingpong, int32_t cus,
         return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "waves_per_simd must be 1, 2 or 3");
     if (pingpong != 0 && (pingpong != 1 || waves_per_simd != 2))
         return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "pingpong must be 0, or 1 with waves_per_simd 2");
-    if (cus < 1 || cus > 65536 || iters < 1 || iters > (1 << 24))
-        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cus must be in 1..65536 and iters in 1..2^24");
+    if (cus < 1 || cus > 65536 || iters < 1 || iters > (1 << 20))
+        return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cus must be in 1..65536 and iters in 1..2^20");
     if (!cycles || !sink || reinterpret_cast<uintptr_t>(cycles) % 8 || reinterpret_cast<uintptr_t>(sink) % 4)
         return fail(nullptr, SPARSE_ATTN_INVALID_ARG, "cycles and sink must be non-null and aligned");
     const hipError_t e = sa::launch_mix_probe(waves_per_simd, pingpong, cus, iters,

@@ -510,7 +510,8 @@ int sparse_attn_mask_info(sparse_attn_handle *h, int64_t *nnz, int32_t *overflow
  *   pingpong 1 (waves_per_simd must be 2): cus workgroups of 8 waves, two
  *     per SIMD, waves 4-7 half a step behind waves 0-3 through one extra
  *     barrier, two barriers per stage (the pair kernel's schedule).
- *   waves_per_simd: 1, 2 or 3; cus: 1..65536; iters: 1..2^24;
+ *   waves_per_simd: 1, 2 or 3; cus: 1..65536; iters: 1..2^20 (a launch of
+ *     2^20 stages runs for a few seconds);
  *   cycles: device int64 [cus * waves_per_simd * 4], out: each wave's
  *     shader-clock cycles over its loop (s_memtime);
  *   sink: device fp32 [cus * waves_per_simd * 256], out: a per-lane sum of

@@ -296,7 +296,7 @@ def test_noalloc_forward_refuses_layouts_beyond_its_scratch(sa):
 
 
 @pytest.mark.parametrize("waves,cus,iters", [(0, 256, 10), (4, 256, 10), (2, 0, 10), (2, 256, 0),
-                                             (2, 256, (1 << 24) + 1)])
+                                             (2, 256, (1 << 20) + 1)])
 def test_mix_probe_rejects_bad_sizes(sa, waves, cus, iters):
     with pytest.raises(sa.SparseAttnError) as e:
         sa.sparse_attn_mix_probe(waves, cus, iters, 1 << 20, 1 << 21, stream=0)
