@@ -15,9 +15,11 @@
 //    lists, so a key tile kept by both is loaded once for 256 queries; each
 //    list entry says which of the two keeps it, and a group skips the math
 //    of entries its tile does not keep.
-//  - Ping-pong: each SIMD hosts one wave of each group, and B runs half a
-//    step behind A, so in every phase one of the two issues matrix products
-//    while the other runs its exponentials (schedule in the kernel body).
+//  - Ping-pong: each SIMD hosts one wave of each group; A's step runs its
+//    matrix products and then its softmax, B's step the softmax of the
+//    previous stage and then its products, so while one of the two issues
+//    matrix products the other runs its exponentials, with one workgroup
+//    barrier per step (schedule in the kernel body).
 //  - Keys are consumed in stages of 64 (half a key tile).  K and the
 //    transposed V tile of a stage are copied global -> LDS by the DMA path
 //    (buffer_load_dwordx4 ... lds: no registers, no LDS store instructions)
@@ -306,20 +308,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
 
     // Ping-pong schedule.  Group A (waves 0-3, first query tile) and group B
     // (waves 4-7, second tile) share the stages; each SIMD hosts one wave of
-    // each.  Every wave runs the same steps, one per stage s:
+    // each.  Step s, one workgroup barrier at its top:
     //
-    //   [barrier] O += P V (s-1), S = K Q^T (s)   [barrier] softmax (s)
+    //   A: [barrier] O += P V (s-1), S = K Q^T (s), copies, softmax (s)
+    //   B: [barrier] copies, softmax (s-1), O += P V (s-1), S = K Q^T (s)
     //
-    // but B passes one extra barrier first, so it runs half a step behind A:
-    // while one wave of a SIMD issues matrix products the other runs its
-    // exponentials.  Stage t lives in ring slot t % 4; its K is read in A's
-    // and then B's step t, its V^T in their steps t + 1.  Each wave copies
-    // its share of stage s + 2 (K by group A, V^T by group B, BPW blocks per
-    // wave) in the softmax half of its step s, into the slot of stage s - 2,
-    // which B finished with in its step s - 1.  At the top of step s a
-    // wave waits for its copies of stage s (those of s + 1 may still fly):
-    // for A that is K(s), needed now; for B, V^T(s), first needed in A's
-    // step s + 1, which starts after B's step s began.
+    // so while one wave of a SIMD issues matrix products the other runs its
+    // exponentials (B's scores of stage s wait in registers for its next
+    // step).  Both groups read K(s) and V^T(s-1) in step s; stage t lives in
+    // ring slot t % 4.  Each wave copies its share of stage s + 2 (K by group
+    // A, V^T by group B, BPW blocks per wave) in step s, into the slot of
+    // stage s - 2, whose K was read in step s - 2 and V^T in step s - 1.  At
+    // the top of step s a wave waits for its copies of stage s (those of
+    // s + 1 may still fly): K(s) is read in step s, V^T(s) in step s + 1.
+    // Both groups run the same steps and leave after the same one, so they
+    // pass the same barriers.
     // Descriptors: kv | bits << 8 | 1 << 10 (0: no such stage).
     int d0, d1;
     {
@@ -337,60 +340,94 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mfma_kernel(Layout L, AttnPa
     Scores S;
     Probs Pr;
     // Step s: K(s) in Kc, V^T(s-1) in Vp; stage s+2 is taken and copied to
-    // Kn, Vn at the start of the softmax phase, which has room for the
-    // scalar work and the copy issue while the other group's wave keeps the
-    // matrix core busy.  Returns whether stage s existed (otherwise the step
-    // only finished s-1).  The slots are distinct arrays addressed statically, so
-    // the compiler can tell the reads of one slot from the copies in flight
-    // to the others.
-    auto step = [&](const char *Kc, const char *Vp, char *Kn, char *Vn, int dprev, int dcur,
-                    int &dnext) {
-        // Hide the operand offsets from loop-invariant hoisting: otherwise
-        // the compiler keeps a full set of addresses per slot live across
-        // the loop and runs out of registers.  Recomputing them costs one
-        // add per offset per step.
+    // Kn, Vn before the softmax, which has room for the scalar work and the
+    // copy issue while the other group's wave keeps the matrix core busy.
+    // A step returns whether stage s existed (otherwise it only finished
+    // s-1).  The slots are distinct arrays addressed statically, so the
+    // compiler can tell the reads of one slot from the copies in flight to
+    // the others.  Each group has its own copy of the loop, so the scores
+    // B keeps across the barrier and the probabilities A keeps across it do
+    // not share a register allocation.
+    //
+    // Hide the operand offsets from loop-invariant hoisting: otherwise the
+    // compiler keeps a full set of addresses per slot live across the loop
+    // and runs out of registers.  Recomputing them costs one add per offset
+    // per step.
+    auto hide = [&]() {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             asm volatile("" : "+v"(kofs[ks]));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             asm volatile("" : "+v"(vofs[q]));
+    };
+    auto copy = [&](char *Kn, char *Vn, int &dnext) {
+        int src;
+        dnext = take(src);
+#pragma unroll
+        for (int t = 0; t < BPW; ++t)
+            issue_block<D>(plan, Kn, Vn, src, wave, t);
+    };
+    auto step_a = [&](const char *Kc, const char *Vp, char *Kn, char *Vn, int dprev, int dcur, int &dnext) {
+        hide();
         wait_vmcnt<BPW>();
         lds_barrier();
         if (attends(dprev))
             pv_stage<D>(Vp, [&](int q) { return vofs[q]; }, Pr, dprev & 255, st);
         if (attends(dcur))
             qk_stage<D>(S, Kc, qf, [&](int ks) { return kofs[ks]; }, dcur & 255, hi);
-        lds_barrier();
-        int src;
-        dnext = take(src);
-#pragma unroll
-        for (int t = 0; t < BPW; ++t)
-            issue_block<D>(plan, Kn, Vn, src, wave, t);
+        copy(Kn, Vn, dnext);
         if (attends(dcur))
             online_softmax<D>(Pr, S, dcur & 255, sl2, st);
         return dcur != 0;
     };
-    if (side == 1)
+    auto step_b = [&](const char *Kc, const char *Vp, char *Kn, char *Vn, int dprev, int dcur, int &dnext) {
+        hide();
+        wait_vmcnt<BPW>();
         lds_barrier();
+        copy(Kn, Vn, dnext);
+        if (attends(dprev)) {
+            online_softmax<D>(Pr, S, dprev & 255, sl2, st);
+            pv_stage<D>(Vp, [&](int q) { return vofs[q]; }, Pr, dprev & 255, st);
+        }
+        if (attends(dcur))
+            qk_stage<D>(S, Kc, qf, [&](int ks) { return kofs[ks]; }, dcur & 255, hi);
+        return dcur != 0;
+    };
     int dm1 = 0;
-    for (;;) {
-        int d2;
-        if (!step(K0, V3, K2, V2, dm1, d0, d2))
-            break;
-        dm1 = d0, d0 = d1, d1 = d2;
-        if (!step(K1, V0, K3, V3, dm1, d0, d2))
-            break;
-        dm1 = d0, d0 = d1, d1 = d2;
-        if (!step(K2, V1, K0, V0, dm1, d0, d2))
-            break;
-        dm1 = d0, d0 = d1, d1 = d2;
-        if (!step(K3, V2, K1, V1, dm1, d0, d2))
-            break;
-        dm1 = d0, d0 = d1, d1 = d2;
+    if (side == 0) {
+        for (;;) {
+            int d2;
+            if (!step_a(K0, V3, K2, V2, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_a(K1, V0, K3, V3, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_a(K2, V1, K0, V0, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_a(K3, V2, K1, V1, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+        }
+    } else {
+        for (;;) {
+            int d2;
+            if (!step_b(K0, V3, K2, V2, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_b(K1, V0, K3, V3, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_b(K2, V1, K0, V0, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+            if (!step_b(K3, V2, K1, V1, dm1, d0, d2))
+                break;
+            dm1 = d0, d0 = d1, d1 = d2;
+        }
     }
-    if (side == 0)
-        lds_barrier();  // pairs with B's extra barrier: both groups pass the same count
     wait_vmcnt<0>();  // no copy may land after the workgroup ends
 
     finish_rows<D>(st, wave_active, lse_at, q_io ? Op + qrow * D : nullptr, hi);
