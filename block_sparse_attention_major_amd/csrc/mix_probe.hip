@@ -17,10 +17,10 @@
 //    holds; as in the row kernel, one barrier per stage, operands read
 //    inline, issue priority raised for the softmax;
 //  - ping-pong: one workgroup of 8 waves per compute unit, two per SIMD, in
-//    the pair kernel's schedule: waves 4-7 pass one extra barrier first, so
-//    they run half a step behind waves 0-3, and a step is [barrier]
-//    O^T += V^T P^T (previous stage), S^T = K Q^T [barrier] softmax; while
-//    one wave of a SIMD issues products the other runs its softmax; the
+//    the pair kernel's schedule, one barrier per step: waves 0-3 run
+//    O^T += V^T P^T (previous stage), S^T = K Q^T, then the softmax; waves
+//    4-7 the softmax of the previous stage, then their products; so while
+//    one wave of a SIMD issues products the other runs its softmax.  The
 //    products are the pair kernel's own (mfma::qk_stage, mfma::pv_stage).
 //
 // Operands are pseudo-random bf16 values in [-1, 1) (an integer hash of
@@ -163,9 +163,9 @@ __global__ __launch_bounds__(256, W) void mix_kernel(int iters, long long *cycle
         cycles[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
 }
 
-// The pair kernel's ping-pong: 8 waves, a step is [barrier] O^T += V^T P^T
-// (previous stage), S^T = K Q^T [barrier] softmax, with waves 4-7 one
-// barrier behind waves 0-3.
+// The pair kernel's ping-pong: 8 waves, one barrier per step; waves 0-3 run
+// products then softmax, waves 4-7 the previous stage's softmax then their
+// products.
 __global__ __launch_bounds__(512, 1) void mix_pingpong_kernel(int iters, long long *cycles, float *sink)
 {
     __shared__ __attribute__((aligned(1024))) char stage[kStageBytes];
@@ -180,19 +180,29 @@ __global__ __launch_bounds__(512, 1) void mix_pingpong_kernel(int iters, long lo
     Scores S;
 
     const long long t0 = (long long)__builtin_amdgcn_s_memtime();
-    if (group == 1)
-        fenced_barrier();  // half a step behind group 0
-    for (int it = 0; it < iters; ++it) {
+    if (group == 0) {
+        for (int it = 0; it < iters; ++it) {
+            fenced_barrier();
+            if (it > 0)
+                pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
+            qk_stage<kD>(S, Ks, w.qf, [&](int ks) { return w.kofs[ks]; }, kStage, hi);
+            online_softmax<kD>(P, S, kStage, sl2, w.st);
+        }
         fenced_barrier();
-        if (it > 0)
-            pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
-        qk_stage<kD>(S, Ks, w.qf, [&](int ks) { return w.kofs[ks]; }, kStage, hi);
-        fenced_barrier();
+        pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
+    } else {
+        for (int it = 0; it < iters; ++it) {
+            fenced_barrier();
+            if (it > 0) {
+                online_softmax<kD>(P, S, kStage, sl2, w.st);
+                pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
+            }
+            qk_stage<kD>(S, Ks, w.qf, [&](int ks) { return w.kofs[ks]; }, kStage, hi);
+        }
+        fenced_barrier();  // both groups pass iters + 1 barriers
         online_softmax<kD>(P, S, kStage, sl2, w.st);
+        pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
     }
-    if (group == 0)
-        fenced_barrier();  // every wave passes 2 iters + 1 barriers
-    pv_stage<kD>(Vs, [&](int q) { return w.vofs[q]; }, P, kStage, w.st);
     const long long t1 = (long long)__builtin_amdgcn_s_memtime();
     sink[blockIdx.x * 512 + tid] = wave_sum(w);
     if (lane == 0)
