@@ -26,7 +26,7 @@ from gpu_helpers import as_f64, assert_close, assert_lse_close, dev, host, lse_b
 
 pytestmark = pytest.mark.gpu
 
-CASES = 60
+CASES = 200
 
 
 def _draw(i):
