@@ -222,6 +222,28 @@ def window_search(sa, wl, q, k, v, stream, tau=0.9):
                     "host greedy dual-window search per head, attention stage under the searched mask"}
 
 
+def copy_reference(stream, nbytes=1 << 30, reps=10):
+    """A plain device-to-device copy of nbytes (torch copy_) on the same GPU:
+    what a streaming read + write sustains here, as context for the HBM-bound
+    permute stages' fraction of the published 8 TB/s.  Bytes counted: read
+    plus written."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    gbs = 2.0 * nbytes / (ms * 1e-3) / 1e9
+    return {"bytes": nbytes, "ms": ms, "gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS}
+
+
 def gemm_reference(stream, n=16384, reps=5):
     """A dense bf16 library GEMM (torch.matmul, n x n x n) on the same GPU:
     what a plain matrix product sustains here under the same power and clock
@@ -348,7 +370,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip the all-ones-mask comparison")
     ap.add_argument("--no-search", action="store_true", help="skip the window-search measurement")
-    ap.add_argument("--no-gemm-reference", action="store_true", help="skip the library GEMM reference")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the library GEMM and device-copy references")
     ap.add_argument("--no-mix-ceiling", action="store_true",
                     help="skip the instruction-mix probe (attention stage mix, no memory traffic)")
     ap.add_argument("--no-order-comparison", action="store_true",
@@ -525,6 +548,7 @@ def main():
     del sel_bitmap, scope_keep
 
     gemm = None if args.no_gemm_reference else gemm_reference(stream)
+    copy_ref = None if args.no_gemm_reference else copy_reference(stream)
     mix = None if args.no_mix_ceiling else mix_ceiling(sa, stream)
     searched = None
     if not args.no_search:
@@ -594,6 +618,7 @@ def main():
                        "unpermute_o_standalone": 2 * in_bytes / (unperm_ms * 1e-3) / 1e9,
                        "mask_compile": mask_buf.numel() / (mask_ms * 1e-3) / 1e9,
                        "peak": PEAK_HBM_GBS,
+                       "device_copy_reference": copy_ref,
                        "note": "unpermute: real rows read + written, timed outside the step (the step "
                                "fuses it); mask compile: bytes of the compiled-mask buffer per call, "
                                "a launch- and latency-bound integer stage"},
